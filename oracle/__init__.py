@@ -1,0 +1,161 @@
+"""FP64 CPU oracle for skip-softmax block-sparse attention — test infrastructure.
+
+Only the tests, ``__graft_entry__.smoke()`` and the bench's ``cpu_baseline``
+leg may import this package.  The product path (``block_sparse_attention_flash_amd``)
+never does, and this package never imports the product.
+
+The arithmetic lives in ``blasst_oracle.c`` (plain C, double precision, one
+OpenMP thread per unit); this file only builds/loads that library and
+marshals numpy arrays.  Inputs are bf16 bit patterns (uint16 numpy arrays),
+exactly the bytes the GPU reads.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "blasst_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+                               "-Wall", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i, dbl = ctypes.c_int, ctypes.c_double
+        lib.oracle_prefill.argtypes = [P, P, P, i, i, i, i, i, i, i, dbl, i, P, i, P, P, P, P, P, i]
+        lib.oracle_prefill.restype = i
+        lib.oracle_decode.argtypes = [P, P, P, i, i, i, i, i, i, dbl, i, P, i, P, P, P, P, P, P, P, i]
+        lib.oracle_decode.restype = i
+        lib.oracle_combine.argtypes = [P, P, i, i, i, P, P]
+        lib.oracle_combine.restype = i
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _u16(a: np.ndarray) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint16:
+        raise TypeError("oracle inputs are bf16 bit patterns (uint16), got %s" % a.dtype)
+    return a
+
+
+def _threads(n):
+    return n if n else min(16, len(os.sched_getaffinity(0)))
+
+
+def prefill(q, k, v, Bc: int, lam: float, causal: bool = True, Br: Optional[int] = None,
+            units: Optional[Sequence[int]] = None, force: Optional[np.ndarray] = None,
+            threads: Optional[int] = None) -> dict:
+    """Blockwise causal prefill.  q [B,Hq,T,d], k/v [B,Hkv,T,d] (bf16 bits).
+
+    units: query-block units (b*Hq + hq)*nq + i to compute (default: all).
+    Returns per-unit arrays o [U,Br,d], lse [U,Br], mask [U,nk] (0 kept /
+    1 skipped / 2 not visited), margin [U,nk] (skipped iff < 0); with all
+    units also o_full [B,Hq,T,d], lse_full [B,Hq,T], mask_full [B,Hq,nq,nk].
+    """
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    B, Hq, T, d = q.shape
+    Hkv = k.shape[1]
+    Br = Br or Bc
+    nq, nk = -(-T // Br), -(-T // Bc)
+    all_units = units is None
+    units = np.arange(B * Hq * nq, dtype=np.int64) if all_units else np.asarray(units, np.int64)
+    U = len(units)
+    o = np.full((U, Br, d), np.nan)
+    lse = np.full((U, Br), np.nan)
+    mask = np.empty((U, nk), np.uint8)
+    margin = np.empty((U, nk))
+    f = None if force is None else np.ascontiguousarray(force, np.int8).reshape(U, nk)
+    rc = _load().oracle_prefill(_ptr(q), _ptr(k), _ptr(v), B, Hq, Hkv, T, d, Bc, Br, float(lam),
+                                int(causal), _ptr(units), U, _ptr(f), _ptr(o), _ptr(lse),
+                                _ptr(mask), _ptr(margin), _threads(threads))
+    if rc:
+        raise ValueError("oracle_prefill rejected its arguments")
+    out = dict(o=o, lse=lse, mask=mask, margin=margin, units=units)
+    if all_units:
+        out["o_full"] = o.reshape(B, Hq, nq * Br, d)[:, :, :T]
+        out["lse_full"] = lse.reshape(B, Hq, nq * Br)[:, :, :T]
+        out["mask_full"] = mask.reshape(B, Hq, nq, nk)
+        out["margin_full"] = margin.reshape(B, Hq, nq, nk)
+    return out
+
+
+def decode(q, k, v, Bc: int, lam: float, num_splits: int,
+           units: Optional[Sequence[int]] = None, force: Optional[np.ndarray] = None,
+           threads: Optional[int] = None) -> dict:
+    """Split-KV decode.  q [B,Hq,1,d], k/v [B,Hkv,N,d] (bf16 bits).
+
+    units: kv-head units b*Hkv + hkv (default: all).  Returns per-unit
+    o_part [U,G,S,d], lse_part [U,G,S], skip [U,G,nk], vskip [U,nk],
+    margin [U,G,nk], vmargin [U,nk]; with all units also the same arrays in
+    [B,Hq,...] / [B,Hkv,...] form under *_full keys.
+    """
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    B, Hq, one, d = q.shape
+    assert one == 1
+    Hkv, N = k.shape[1], k.shape[2]
+    G, S, nk = Hq // Hkv, num_splits, -(-N // Bc)
+    all_units = units is None
+    units = np.arange(B * Hkv, dtype=np.int64) if all_units else np.asarray(units, np.int64)
+    U = len(units)
+    o_part = np.full((U, G, S, d), np.nan)
+    lse_part = np.full((U, G, S), np.nan)
+    skip = np.empty((U, G, nk), np.uint8)
+    vskip = np.empty((U, nk), np.uint8)
+    margin = np.empty((U, G, nk))
+    vmargin = np.empty((U, nk))
+    f = None if force is None else np.ascontiguousarray(force, np.int8).reshape(U, G, nk)
+    rc = _load().oracle_decode(_ptr(q), _ptr(k), _ptr(v), B, Hq, Hkv, N, d, Bc, float(lam), S,
+                               _ptr(units), U, _ptr(f), _ptr(o_part), _ptr(lse_part), _ptr(skip),
+                               _ptr(vskip), _ptr(margin), _ptr(vmargin), _threads(threads))
+    if rc:
+        raise ValueError("oracle_decode rejected its arguments")
+    out = dict(o_part=o_part, lse_part=lse_part, skip=skip, vskip=vskip, margin=margin,
+               vmargin=vmargin, units=units)
+    if all_units:
+        out["o_part_full"] = o_part.reshape(B, Hq, S, d)
+        out["lse_part_full"] = lse_part.reshape(B, Hq, S)
+        out["skip_full"] = skip.reshape(B, Hq, nk)
+        out["vskip_full"] = vskip.reshape(B, Hkv, nk)
+        out["margin_full"] = margin.reshape(B, Hq, nk)
+        out["vmargin_full"] = vmargin.reshape(B, Hkv, nk)
+    return out
+
+
+def combine(o_part: np.ndarray, lse_part: np.ndarray):
+    """Log-sum-exp merge over the split axis: o_part [..., S, d], lse_part [..., S]."""
+    lead = o_part.shape[:-2]
+    S, d = o_part.shape[-2:]
+    rows = int(np.prod(lead)) if lead else 1
+    op = np.ascontiguousarray(o_part, np.float64).reshape(rows, S, d)
+    lp = np.ascontiguousarray(lse_part, np.float64).reshape(rows, S)
+    o = np.empty((rows, d))
+    lse = np.empty(rows)
+    rc = _load().oracle_combine(_ptr(op), _ptr(lp), rows, S, d, _ptr(o), _ptr(lse))
+    if rc:
+        raise ValueError("oracle_combine rejected its arguments")
+    return o.reshape(*lead, d), lse.reshape(lead)
