@@ -1,0 +1,261 @@
+#!/usr/bin/env python3
+"""Benchmark of skip-softmax block-sparse attention on one MI355X.
+
+One step = one split-KV decode step at 32K context (Llama-3.1-8B-like layer:
+B=1, Hq=32, Hkv=8, d=128, N=32768, Bc=128, lambda=1e-3, 16 splits) followed by
+the log-sum-exp combine, on seeded synthetic heavy-tailed inputs.  The KV cache
+is rotated over several identical copies so the working set exceeds twice the
+256 MB Infinity Cache and every step reads from HBM.
+
+Printed: one JSON line whose `value` is the decode step's algorithmic HBM
+throughput (GB/s: all of K, the kept V blocks, q, the split partials and the
+decision bytes, divided by the step time), plus the decode split kernel's
+roofline (its algorithmic bytes per launch over its average launch duration
+from HIP events on the launch stream), the 32K causal prefill's executed
+TFLOP/s at lambda in {1e-4, 1e-3, 1e-2} and the dense (lambda = 0) reference,
+block sparsity, and the FP64 oracle timed on this host as a CPU baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "decode µs & HBM GB/s at 32K; prefill TFLOP/s at 32K; block sparsity %"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--copies", type=int, default=4, help="KV copies rotated to defeat the Infinity Cache")
+    p.add_argument("--prefill-reps", type=int, default=5)
+    p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    return p.parse_args()
+
+
+def dev(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def decode_bytes(w, vskip: np.ndarray):
+    """Algorithmic bytes of one split-kernel launch and of one combine launch."""
+    B, Hq, Hkv, N, d, Bc, S = w.B, w.Hq, w.Hkv, w.T, w.d, w.Bc, w.num_splits
+    nk = -(-N // Bc)
+    rows_per_block = np.minimum(Bc, N - np.arange(nk) * Bc)
+    kept_rows = int(((vskip == 0) * rows_per_block[None, None, :]).sum())
+    k_bytes = B * Hkv * N * d * 2
+    v_bytes = kept_rows * d * 2
+    q_bytes = B * Hq * d * 2
+    part_bytes = B * Hq * S * (d + 1) * 4
+    mask_bytes = B * Hq * nk + B * Hkv * nk
+    split = k_bytes + v_bytes + q_bytes + part_bytes + mask_bytes
+    combine = part_bytes + B * Hq * (d + 1) * 4
+    return dict(split=split, combine=combine, k=k_bytes, v_kept=v_bytes, v_dense=B * Hkv * N * d * 2)
+
+
+def bench_decode(args, lib, torch, W):
+    w = W.CONFIGS["decode_32k"]
+    lam = w.lambdas[0]
+    x = W.generate(w)
+    copies = [{k: dev(v) for k, v in x.items()} for _ in range(max(1, args.copies))]
+    B, Hq, N, d, Bc, S = w.B, w.Hq, w.T, w.d, w.Bc, w.num_splits
+    nk = -(-N // Bc)
+    f32 = dict(dtype=torch.float32, device="cuda")
+    o_part = torch.empty((B, Hq, S, d), **f32)
+    lse_part = torch.empty((B, Hq, S), **f32)
+    o = torch.empty((B, Hq, d), **f32)
+    lse = torch.empty((B, Hq), **f32)
+    skip = torch.empty((B, Hq, nk), dtype=torch.uint8, device="cuda")
+    vskip = torch.empty((B, w.Hkv, nk), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+
+    def split_args(c, lam_):
+        return (P(c["q"]), P(c["k"]), P(c["v"]), P(o_part), P(lse_part), P(skip), P(vskip),
+                B, Hq, N, d, w.G, Bc, ctypes.c_double(lam_), 1, S, sp)
+
+    comb = (P(o_part), P(lse_part), P(o), P(lse), B, Hq, d, S, sp)
+    sargs = [split_args(c, lam) for c in copies]
+    dense_args = [split_args(c, 0.0) for c in copies]
+    decode_fn, combine_fn = lib.blasst_decode, lib.blasst_decode_combine
+
+    def check(st):
+        if st != 0:
+            raise RuntimeError("libblasst call failed with status %d" % st)
+
+    for s in range(args.warmup):
+        check(decode_fn(*sargs[s % len(sargs)]))
+        check(combine_fn(*comb))
+    torch.cuda.synchronize()
+
+    # timed region: K steps; events bracket every split launch on the launch stream
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        check(decode_fn(*sargs[s % len(sargs)]))
+        ev[s][1].record(stream)
+        check(combine_fn(*comb))
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = start.elapsed_time(stop) / args.steps
+    split_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    # dense-equivalent reference (lambda = 0): same kernels, nothing skipped
+    for s in range(args.warmup):
+        check(decode_fn(*dense_args[s % len(dense_args)]))
+    torch.cuda.synchronize()
+    start.record(stream)
+    for s in range(args.steps):
+        check(decode_fn(*dense_args[s % len(dense_args)]))
+        check(combine_fn(*comb))
+    stop.record(stream)
+    torch.cuda.synchronize()
+    dense_step_ms = start.elapsed_time(stop) / args.steps
+
+    # decisions of the timed configuration (identical on every copy)
+    check(decode_fn(*sargs[0]))
+    torch.cuda.synchronize()
+    sk, vsk = skip.cpu().numpy(), vskip.cpu().numpy()
+    by = decode_bytes(w, vsk)
+    return dict(w=w, x=x, step_ms=step_ms, split_ms=split_ms, dense_step_ms=dense_step_ms, wall=wall,
+                bytes=by, block_sparsity=float(sk.mean()), vload_sparsity=float(vsk.mean()))
+
+
+def bench_prefill(args, lib, torch, W):
+    w = W.CONFIGS["prefill_32k"]
+    x = {k: dev(v) for k, v in W.generate(w).items()}
+    B, Hq, T, d, Bc = w.B, w.Hq, w.T, w.d, w.Bc
+    nq = -(-T // Bc)
+    o = torch.empty((B, Hq, T, d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device="cuda")
+    mask = torch.empty((B, Hq, nq, nq), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    out = {}
+    visited = B * Hq * nq * (nq + 1) // 2
+    tile_flops = 2.0 * Bc * Bc * d
+    for lam in (0.0,) + tuple(w.lambdas):
+        a = (P(x["q"]), P(x["k"]), P(x["v"]), P(o), P(lse), P(mask), B, Hq, T, d, w.G, Bc,
+             ctypes.c_double(lam), 1, ctypes.c_void_p(stream.cuda_stream))
+        for _ in range(2):
+            assert lib.blasst_prefill(*a) == 0
+        torch.cuda.synchronize()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        for _ in range(args.prefill_reps):
+            assert lib.blasst_prefill(*a) == 0
+        s1.record(stream)
+        torch.cuda.synchronize()
+        ms = s0.elapsed_time(s1) / args.prefill_reps
+        m = mask.cpu().numpy()
+        skipped = int((m == 1).sum())
+        kept = visited - skipped
+        flops = (visited + kept) * tile_flops
+        tflops = flops / (ms * 1e-3) / 1e12
+        out["%g" % lam] = dict(ms=round(ms, 4), tflops_executed=round(tflops, 2),
+                               frac_of_mfma_peak=round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                               block_sparsity=round(skipped / visited, 5),
+                               executed_tflop=round(flops / 1e12, 4))
+    dense = out["0"]["ms"]
+    for k, v in out.items():
+        v["speedup_vs_lambda0"] = round(dense / v["ms"], 4)
+    return dict(workload=w.name, B=B, Hq=Hq, Hkv=w.Hkv, d=d, T=T, Bc=Bc, by_lambda=out)
+
+
+def cpu_baseline(args, dres):
+    import oracle
+    w = dres["w"]
+    x = dres["x"]
+    threads = min(16, len(os.sched_getaffinity(0)))
+    oracle.decode(x["q"], x["k"], x["v"], w.Bc, w.lambdas[0], w.num_splits, threads=threads)  # warm
+    n, t0 = 0, time.perf_counter()
+    while True:
+        r = oracle.decode(x["q"], x["k"], x["v"], w.Bc, w.lambdas[0], w.num_splits, threads=threads)
+        oracle.combine(r["o_part_full"], r["lse_part_full"])
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= args.cpu_seconds:
+            break
+    per = el / n
+    by = decode_bytes(w, r["vskip_full"])
+    gbs = (by["split"] + by["combine"]) / per / 1e9
+    return dict(value=round(gbs, 4), unit="GB/s", cores=threads, kind="oracle",
+                sample="full decode_32k step (all 32 heads, 16 splits) + combine, repeated %d times in %.1f s; "
+                       "%.1f ms per step" % (n, el, per * 1e3))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus %d)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import block_sparse_attention_flash_amd as bsa
+    import workloads as W
+    torch.cuda.set_device(0)
+    lib = bsa._load()
+
+    d = bench_decode(args, lib, torch, W)
+    pre = None if args.no_prefill else bench_prefill(args, lib, torch, W)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args, d)
+
+    by = d["bytes"]
+    step_bytes = by["split"] + by["combine"]
+    value = step_bytes / (d["step_ms"] * 1e-3) / 1e9
+    achieved = by["split"] / (d["split_ms"] * 1e-3) / 1e9
+    w = d["w"]
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(d["step_ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "kind": "split-KV decode + LSE combine", "B": w.B, "Hq": w.Hq,
+                   "Hkv": w.Hkv, "d": w.d, "context": w.T, "Bc": w.Bc, "lambda": w.lambdas[0],
+                   "num_splits": w.num_splits, "kv_copies_rotated": args.copies},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode_split_kernel", "bytes_per_launch": by["split"],
+                     "avg_launch_us": round(d["split_ms"] * 1e3, 3)},
+        "decode": {"step_us": round(d["step_ms"] * 1e3, 3), "split_kernel_us": round(d["split_ms"] * 1e3, 3),
+                   "dense_step_us": round(d["dense_step_ms"] * 1e3, 3),
+                   "speedup_vs_lambda0": round(d["dense_step_ms"] / d["step_ms"], 4),
+                   "block_sparsity": round(d["block_sparsity"], 5), "vload_sparsity": round(d["vload_sparsity"], 5),
+                   "bytes": by},
+        "prefill": pre,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,196 @@
+"""Skip-softmax (BLASST) block-sparse attention on AMD Instinct MI355X.
+
+A thin ctypes binding over ``libblasst.so`` (C ABI in ``include/blasst.h``).
+The functions named like the C entry points take PyTorch tensors that already
+live on the GPU and only marshal pointers, sizes and the current HIP stream;
+every step of the computation runs in the library's HIP kernels.  If the
+library is missing or fails to load, importing the binding's functions raises:
+there is no CPU or PyTorch fallback.
+
+The convenience wrappers ``prefill``, ``decode`` and ``decode_combine``
+allocate their outputs with PyTorch and call the entry points.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = ["blasst_prefill", "blasst_decode", "blasst_decode_combine", "status_string",
+           "prefill", "decode", "decode_combine", "BlasstError", "library_path", "build"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libblasst.so")
+_lib = None
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_INTERNAL = 0, 1, 2, 3, 4
+
+
+class BlasstError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__("%s failed: %s (status %d)" % (fn, status_string(status), status))
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def build(verbose: bool = False) -> str:
+    """Compile libblasst.so in-tree with hipcc for gfx950."""
+    from . import _build
+    return _build.build(verbose=verbose)
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError("libblasst.so is not built (%s); run "
+                              "`python -m block_sparse_attention_flash_amd._build`" % _LIB_PATH)
+        lib = ctypes.CDLL(_LIB_PATH)
+        P, i, d = ctypes.c_void_p, ctypes.c_int, ctypes.c_double
+        lib.blasst_prefill.argtypes = [P, P, P, P, P, P, i, i, i, i, i, i, d, i, P]
+        lib.blasst_prefill.restype = i
+        lib.blasst_decode.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, i, d, i, i, P]
+        lib.blasst_decode.restype = i
+        lib.blasst_decode_combine.argtypes = [P, P, P, P, i, i, i, i, P]
+        lib.blasst_decode_combine.restype = i
+        lib.blasst_status_string.argtypes = [i]
+        lib.blasst_status_string.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return _load().blasst_status_string(int(status)).decode()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream: Optional[torch.cuda.Stream]):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(fn: str, status: int):
+    if status != OK:
+        raise BlasstError(fn, status)
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype):
+    if not (t.is_cuda and t.dtype == dtype and t.is_contiguous()):
+        raise ValueError("%s must be a contiguous %s tensor on the GPU" % (name, dtype))
+
+
+def blasst_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                   lse: Optional[torch.Tensor], skip_mask: Optional[torch.Tensor], Bc: int,
+                   lam: float, causal: bool = True, stream=None) -> None:
+    """q [B,Hq,T,d], k/v [B,Hkv,T,d] bf16; o [B,Hq,T,d] fp32; lse [B,Hq,T] fp32 or None;
+    skip_mask [B,Hq,nq,nq] uint8 or None."""
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, nm, torch.bfloat16)
+    _need(o, "o", torch.float32)
+    B, Hq, T, d = q.shape
+    Hkv = k.shape[1]
+    if Hkv == 0 or Hq % Hkv or k.shape != (B, Hkv, T, d) or v.shape != k.shape or o.shape != q.shape:
+        raise ValueError("inconsistent prefill shapes")
+    nq = -(-T // Bc)
+    if lse is not None:
+        _need(lse, "lse", torch.float32)
+        if lse.shape != (B, Hq, T):
+            raise ValueError("lse must be [B,Hq,T]")
+    if skip_mask is not None:
+        _need(skip_mask, "skip_mask", torch.uint8)
+        if skip_mask.shape != (B, Hq, nq, nq):
+            raise ValueError("skip_mask must be [B,Hq,nq,nq]")
+    st = _load().blasst_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(skip_mask), B, Hq, T, d,
+                                Hq // Hkv, Bc, float(lam), int(bool(causal)), _stream(stream))
+    _check("blasst_prefill", st)
+
+
+def blasst_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o_part: torch.Tensor,
+                  lse_part: torch.Tensor, skip_mask: Optional[torch.Tensor], vskip_mask: Optional[torch.Tensor],
+                  Bc: int, lam: float, num_splits: int, causal: bool = True, stream=None) -> None:
+    """q [B,Hq,1,d], k/v [B,Hkv,N,d] bf16; o_part [B,Hq,S,d], lse_part [B,Hq,S] fp32;
+    skip_mask [B,Hq,nk] / vskip_mask [B,Hkv,nk] uint8 or None."""
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, nm, torch.bfloat16)
+    _need(o_part, "o_part", torch.float32)
+    _need(lse_part, "lse_part", torch.float32)
+    B, Hq, one, d = q.shape
+    Hkv, N = k.shape[1], k.shape[2]
+    S = num_splits
+    if one != 1 or Hkv == 0 or Hq % Hkv or k.shape != (B, Hkv, N, d) or v.shape != k.shape:
+        raise ValueError("inconsistent decode shapes")
+    if o_part.shape != (B, Hq, S, d) or lse_part.shape != (B, Hq, S):
+        raise ValueError("o_part must be [B,Hq,S,d] and lse_part [B,Hq,S]")
+    nk = -(-N // Bc)
+    if skip_mask is not None:
+        _need(skip_mask, "skip_mask", torch.uint8)
+        if skip_mask.shape != (B, Hq, nk):
+            raise ValueError("skip_mask must be [B,Hq,nk]")
+    if vskip_mask is not None:
+        _need(vskip_mask, "vskip_mask", torch.uint8)
+        if vskip_mask.shape != (B, Hkv, nk):
+            raise ValueError("vskip_mask must be [B,Hkv,nk]")
+    st = _load().blasst_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o_part), _ptr(lse_part), _ptr(skip_mask),
+                               _ptr(vskip_mask), B, Hq, N, d, Hq // Hkv, Bc, float(lam), int(bool(causal)), S,
+                               _stream(stream))
+    _check("blasst_decode", st)
+
+
+def blasst_decode_combine(o_part: torch.Tensor, lse_part: torch.Tensor, o: torch.Tensor,
+                          lse: Optional[torch.Tensor], stream=None) -> None:
+    """o_part [B,Hq,S,d], lse_part [B,Hq,S] -> o [B,Hq,d], lse [B,Hq] or None (fp32)."""
+    _need(o_part, "o_part", torch.float32)
+    _need(lse_part, "lse_part", torch.float32)
+    _need(o, "o", torch.float32)
+    B, Hq, S, d = o_part.shape
+    if lse_part.shape != (B, Hq, S) or o.shape != (B, Hq, d):
+        raise ValueError("inconsistent combine shapes")
+    if lse is not None:
+        _need(lse, "lse", torch.float32)
+        if lse.shape != (B, Hq):
+            raise ValueError("lse must be [B,Hq]")
+    st = _load().blasst_decode_combine(_ptr(o_part), _ptr(lse_part), _ptr(o), _ptr(lse), B, Hq, d, S,
+                                       _stream(stream))
+    _check("blasst_decode_combine", st)
+
+
+def prefill(q, k, v, lam: float, Bc: int = 128, causal: bool = True,
+            with_mask: bool = True) -> Tuple[torch.Tensor, torch.Tensor, Optional[torch.Tensor]]:
+    """Allocating wrapper: returns (o fp32 [B,Hq,T,d], lse [B,Hq,T], mask [B,Hq,nq,nq] or None)."""
+    B, Hq, T, d = q.shape
+    nq = -(-T // Bc)
+    o = torch.empty((B, Hq, T, d), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    mask = torch.empty((B, Hq, nq, nq), dtype=torch.uint8, device=q.device) if with_mask else None
+    blasst_prefill(q, k, v, o, lse, mask, Bc, lam, causal)
+    return o, lse, mask
+
+
+def decode(q, k, v, lam: float, num_splits: int, Bc: int = 128, with_masks: bool = True):
+    """Allocating wrapper: returns (o_part, lse_part, skip [B,Hq,nk], vskip [B,Hkv,nk])."""
+    B, Hq, _, d = q.shape
+    Hkv, N = k.shape[1], k.shape[2]
+    nk = -(-N // Bc)
+    o_part = torch.empty((B, Hq, num_splits, d), dtype=torch.float32, device=q.device)
+    lse_part = torch.empty((B, Hq, num_splits), dtype=torch.float32, device=q.device)
+    skip = torch.empty((B, Hq, nk), dtype=torch.uint8, device=q.device) if with_masks else None
+    vskip = torch.empty((B, Hkv, nk), dtype=torch.uint8, device=q.device) if with_masks else None
+    blasst_decode(q, k, v, o_part, lse_part, skip, vskip, Bc, lam, num_splits)
+    return o_part, lse_part, skip, vskip
+
+
+def decode_combine(o_part, lse_part):
+    """Allocating wrapper: returns (o [B,Hq,d], lse [B,Hq])."""
+    B, Hq, S, d = o_part.shape
+    o = torch.empty((B, Hq, d), dtype=torch.float32, device=o_part.device)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=o_part.device)
+    blasst_decode_combine(o_part, lse_part, o, lse)
+    return o, lse

@@ -1,0 +1,135 @@
+// C ABI of libblasst.so (declared in include/blasst.h): host-side argument
+// validation, threshold set-up and kernel dispatch.  Nothing here allocates.
+#include "blasst.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "kernels.h"
+
+#define BLASST_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr double kLog2e = 1.4426950408889634;
+
+bool supported_dim(int x) { return x == 64 || x == 128; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ln(lambda) in log2 units; lambda = 0 never skips.
+float log2_threshold(double lambda) {
+    return lambda > 0.0 ? static_cast<float>(std::log(lambda) * kLog2e) : -INFINITY;
+}
+
+bool lambda_ok(double lambda) { return lambda >= 0.0 && lambda < 1.0; }  // NaN fails both
+
+blasst_status from_hip(hipError_t e) { return e == hipSuccess ? BLASST_OK : BLASST_ERR_HIP; }
+
+}  // namespace
+
+BLASST_EXPORT blasst_status blasst_prefill(const void* q, const void* k, const void* v, float* o, float* lse,
+                                           uint8_t* skip_mask, int B, int Hq, int T, int d, int gqa_ratio,
+                                           int Bc, double lambda, int causal, blasst_stream_t stream) {
+    try {
+        if (B < 0 || Hq < 0 || T < 0 || d <= 0 || Bc <= 0 || gqa_ratio < 1) return BLASST_ERR_INVALID_ARG;
+        if (Hq % gqa_ratio != 0 || !lambda_ok(lambda) || (causal != 0 && causal != 1))
+            return BLASST_ERR_INVALID_ARG;
+        if (!supported_dim(d) || !supported_dim(Bc)) return BLASST_ERR_UNSUPPORTED;
+        if ((int64_t)B * Hq * T == 0) return BLASST_OK;  // nothing to do; pointers are not read
+        if (!q || !k || !v || !o) return BLASST_ERR_INVALID_ARG;
+        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return BLASST_ERR_INVALID_ARG;
+        const int64_t nq = (T + Bc - 1) / Bc;
+        if (nq * B * Hq > INT32_MAX) return BLASST_ERR_UNSUPPORTED;
+
+        blasst::PrefillArgs a;
+        a.q = static_cast<const uint16_t*>(q);
+        a.k = static_cast<const uint16_t*>(k);
+        a.v = static_cast<const uint16_t*>(v);
+        a.o = o;
+        a.lse = lse;
+        a.mask = skip_mask;
+        a.B = B;
+        a.Hq = Hq;
+        a.G = gqa_ratio;
+        a.Hkv = Hq / gqa_ratio;
+        a.T = T;
+        a.nq = (int)nq;
+        a.nk = (int)nq;
+        a.causal = causal;
+        a.score_scale = static_cast<float>(kLog2e / std::sqrt((double)d));
+        a.thr = log2_threshold(lambda);
+        return from_hip(blasst::launch_prefill(a, d, Bc, reinterpret_cast<hipStream_t>(stream)));
+    } catch (...) {
+        return BLASST_ERR_INTERNAL;
+    }
+}
+
+BLASST_EXPORT blasst_status blasst_decode(const void* q, const void* k, const void* v, float* o_part,
+                                          float* lse_part, uint8_t* skip_mask, uint8_t* vskip_mask, int B,
+                                          int Hq, int N, int d, int gqa_ratio, int Bc, double lambda, int causal,
+                                          int num_splits, blasst_stream_t stream) {
+    try {
+        if (B < 0 || Hq < 0 || N <= 0 || d <= 0 || Bc <= 0 || gqa_ratio < 1) return BLASST_ERR_INVALID_ARG;
+        if (Hq % gqa_ratio != 0 || !lambda_ok(lambda) || (causal != 0 && causal != 1))
+            return BLASST_ERR_INVALID_ARG;
+        const int64_t nk = ((int64_t)N + Bc - 1) / Bc;
+        if (num_splits < 1 || num_splits > nk) return BLASST_ERR_INVALID_ARG;
+        if (!supported_dim(d) || !supported_dim(Bc)) return BLASST_ERR_UNSUPPORTED;
+        if (gqa_ratio > 64) return BLASST_ERR_UNSUPPORTED;  // one workgroup covers at most 64 heads of a group
+        if ((int64_t)B * Hq == 0) return BLASST_OK;  // nothing to do; pointers are not read
+        if (!q || !k || !v || !o_part || !lse_part) return BLASST_ERR_INVALID_ARG;
+        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o_part)) return BLASST_ERR_INVALID_ARG;
+        if (B > 65535 || Hq / gqa_ratio > 65535) return BLASST_ERR_UNSUPPORTED;
+
+        blasst::DecodeArgs a;
+        a.q = static_cast<const uint16_t*>(q);
+        a.k = static_cast<const uint16_t*>(k);
+        a.v = static_cast<const uint16_t*>(v);
+        a.o_part = o_part;
+        a.lse_part = lse_part;
+        a.skip = skip_mask;
+        a.vskip = vskip_mask;
+        a.B = B;
+        a.Hq = Hq;
+        a.G = gqa_ratio;
+        a.Hkv = Hq / gqa_ratio;
+        a.N = N;
+        a.nk = (int)nk;
+        a.S = num_splits;
+        a.score_scale = static_cast<float>(kLog2e / std::sqrt((double)d));
+        a.thr = log2_threshold(lambda);
+        return from_hip(blasst::launch_decode(a, d, Bc, reinterpret_cast<hipStream_t>(stream)));
+    } catch (...) {
+        return BLASST_ERR_INTERNAL;
+    }
+}
+
+BLASST_EXPORT blasst_status blasst_decode_combine(const float* o_part, const float* lse_part, float* o, float* lse,
+                                                  int B, int Hq, int d, int num_splits, blasst_stream_t stream) {
+    try {
+        if (B < 0 || Hq < 0 || d <= 0 || num_splits < 1) return BLASST_ERR_INVALID_ARG;
+        if (!supported_dim(d)) return BLASST_ERR_UNSUPPORTED;
+        const int64_t rows = (int64_t)B * Hq;
+        if (rows == 0) return BLASST_OK;  // nothing to do; pointers are not read
+        if (!o_part || !lse_part || !o) return BLASST_ERR_INVALID_ARG;
+        if (rows > INT32_MAX) return BLASST_ERR_UNSUPPORTED;
+        return from_hip(blasst::launch_decode_combine(o_part, lse_part, o, lse, (int)rows, d, num_splits,
+                                                      reinterpret_cast<hipStream_t>(stream)));
+    } catch (...) {
+        return BLASST_ERR_INTERNAL;
+    }
+}
+
+BLASST_EXPORT const char* blasst_status_string(blasst_status status) {
+    switch (status) {
+        case BLASST_OK: return "ok";
+        case BLASST_ERR_INVALID_ARG: return "invalid argument";
+        case BLASST_ERR_UNSUPPORTED: return "unsupported configuration";
+        case BLASST_ERR_HIP: return "HIP launch or runtime error";
+        case BLASST_ERR_INTERNAL: return "internal error";
+    }
+    return "unknown status";
+}

@@ -1,0 +1,70 @@
+// Device-side building blocks shared by the gfx950 kernels of libblasst.
+//
+// Lane layouts below were checked on MI355X hardware:
+//  * v_mfma_f32_16x16x32_bf16: lane l holds A[l&15][8*(l>>4)+i] and
+//    B[8*(l>>4)+i][l&15] (i = 0..7); the result C[4*(l>>4)+i][l&15] (i = 0..3).
+//  * v_mfma_f32_32x32x16_bf16: lane l holds A[l&31][8*(l>>5)+i] and
+//    B[8*(l>>5)+i][l&31]; the result C[8*(i>>2) + 4*(l>>5) + (i&3)][l&31].
+//  * ds_read_b64_tr_b16: inside each group of 16 lanes, lane 4r+c names 4
+//    consecutive 16-bit values (row r, columns 4c..4c+3 of a 4x16 block) and
+//    lane j receives column j of that block: out[j][e] = block[e][j].
+// Vectors of __bf16 are only ever built or taken apart as whole registers
+// (bit casts of integer vectors); element access on them is avoided.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace blasst {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) char lds_char;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+// 16-byte global load (one global_load_dwordx4).
+__device__ __forceinline__ u32x4 load16(const void* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Two fp32 -> two bf16 (round to nearest even), packed low|high into one dword.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    f32x2 x = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+}
+
+// 2^x on the transcendental unit (v_exp_f32); 2^-inf = 0.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Transposed 8-byte LDS read (see the layout note at the top).
+__device__ __forceinline__ u32x2 lds_read_tr16(const lds_char* p) {
+    i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+    return __builtin_bit_cast(u32x2, r);
+}
+
+__device__ __forceinline__ float wave_shfl_xor(float x, int mask) {
+    return __shfl_xor(x, mask, 64);
+}
+
+}  // namespace blasst

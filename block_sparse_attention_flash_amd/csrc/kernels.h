@@ -1,0 +1,41 @@
+// Internal launch interface between the C ABI (api.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace blasst {
+
+// Split-KV decode launch.  Pointers and sizes already validated by the caller.
+struct DecodeArgs {
+    const uint16_t* q;  // bf16 [B, Hq, 1, d]
+    const uint16_t* k;  // bf16 [B, Hkv, N, d]
+    const uint16_t* v;  // bf16 [B, Hkv, N, d]
+    float* o_part;      // [B, Hq, S, d]
+    float* lse_part;    // [B, Hq, S]
+    uint8_t* skip;      // [B, Hq, nk] or null
+    uint8_t* vskip;     // [B, Hkv, nk] or null
+    int B, Hq, Hkv, G, N, nk, S;
+    float score_scale;  // log2(e) / sqrt(d): scores are handled in log2 units
+    float thr;          // ln(lambda) * log2(e); -inf when lambda == 0
+};
+
+// Causal / full prefill launch.
+struct PrefillArgs {
+    const uint16_t* q;  // bf16 [B, Hq, T, d]
+    const uint16_t* k;  // bf16 [B, Hkv, T, d]
+    const uint16_t* v;  // bf16 [B, Hkv, T, d]
+    float* o;           // [B, Hq, T, d]
+    float* lse;         // [B, Hq, T] or null
+    uint8_t* mask;      // [B, Hq, nq, nk] or null
+    int B, Hq, Hkv, G, T, nq, nk, causal;
+    float score_scale;
+    float thr;
+};
+
+hipError_t launch_decode(const DecodeArgs& a, int d, int Bc, hipStream_t stream);
+hipError_t launch_decode_combine(const float* o_part, const float* lse_part, float* o, float* lse, int rows,
+                                 int d, int S, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, int d, int Bc, hipStream_t stream);
+
+}  // namespace blasst

@@ -1,0 +1,135 @@
+/*
+ * blasst.h — C ABI of libblasst.so: skip-softmax ("BLASST") block-sparse
+ * attention for AMD Instinct MI355X (gfx950).
+ *
+ * The method (BLASST blog, "BLASST: Dynamic BLocked Attention Sparsity via
+ * Softmax Thresholding", MLSys 2026 notes):
+ *   Blockwise online-softmax attention (section on FlashAttention's online
+ *   softmax, Eqs. 1-4) with one extra test (section on the decision rule,
+ *   Eq. 5): for KV block j the kernel forms S = Q K_j^T / sqrt(d), takes the
+ *   block row max mt, updates the running max m_new = max(m, mt), and skips
+ *   the block when mt - m_new < ln(lambda).  A skipped block does no exp, no
+ *   P V product and (in decode) no V load; S itself is always formed (section
+ *   on what a skip saves).  In prefill a block is skipped only if every row of
+ *   the query block votes to skip; in decode each query head decides alone
+ *   (Table 12 discussion under the lambda = a/L section).
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are contiguous, row-major, innermost dimension last, in device
+ *     memory owned by the caller.  q/k/v are bfloat16 (passed as const void*).
+ *     Every pointer must be 16-byte aligned.
+ *   - Query head h reads kv head h / gqa_ratio (Hkv = Hq / gqa_ratio):
+ *     gqa_ratio = 1 is MHA, 1 < gqa_ratio < Hq is GQA, gqa_ratio = Hq is MQA.
+ *   - lambda in [0, 1).  lambda = 0 never skips (dense attention).
+ *   - Scores are scaled by 1/sqrt(d) before the max and the test.
+ *   - Supported: d in {64, 128}, Bc in {64, 128}.  Sequence lengths need not
+ *     be multiples of Bc: the last block is shorter.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream) and return once the kernels are enqueued.  Buffers must stay
+ *     alive until the stream passes that point.  The library allocates no
+ *     memory and keeps no state between calls; concurrent calls on different
+ *     streams are safe.
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     rejected call enqueues nothing.  A launch failure returns BLASST_ERR_HIP.
+ *     No C++ exception crosses this interface.
+ *   - Mask bytes: 0 = block kept, 1 = block skipped, 2 = block not visited
+ *     (prefill, above the causal diagonal).
+ */
+#ifndef BLASST_H
+#define BLASST_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as HIP's hipStream_t. */
+typedef struct ihipStream_t* blasst_stream_t;
+
+typedef enum {
+    BLASST_OK = 0,
+    BLASST_ERR_INVALID_ARG = 1, /* null required pointer, bad size, lambda outside [0,1), ... */
+    BLASST_ERR_UNSUPPORTED = 2, /* valid but not built: d or Bc outside {64,128}, ... */
+    BLASST_ERR_HIP = 3,         /* a HIP launch or runtime call failed */
+    BLASST_ERR_INTERNAL = 4
+} blasst_status;
+
+/*
+ * Causal (or full) GQA prefill.  The blog's prefill kernel: every KV tile's
+ * S = Q K^T is computed; a tile whose Bc query rows all vote to skip does no
+ * exp, row sum or P V (section on the prefill kernel; query block height
+ * Br = Bc).
+ *
+ *   q          bf16 [B, Hq,  T, d]
+ *   k, v       bf16 [B, Hkv, T, d]       Hkv = Hq / gqa_ratio
+ *   o          fp32 [B, Hq,  T, d]       output rows O / l
+ *   lse        fp32 [B, Hq,  T] or NULL  natural-log m + ln(l) per row
+ *   skip_mask  u8   [B, Hq, ceil(T/Bc), ceil(T/Bc)] or NULL; entry (i, j) is the
+ *              decision for query block i and KV block j (0/1), or 2 when
+ *              causal and j > i.  Every entry is written.
+ *   causal     1: row t sees keys <= t.  0: every row sees every key.
+ * Errors: INVALID_ARG for a null q/k/v/o, B/Hq/T < 0, d/Bc <= 0, gqa_ratio < 1
+ * or not dividing Hq, lambda outside [0,1) or NaN, causal not 0/1;
+ * UNSUPPORTED for d or Bc outside {64, 128}.  Scalar arguments are checked
+ * first; then B*Hq*T == 0 returns OK and does nothing (the pointers may then be
+ * NULL and are not read).
+ */
+blasst_status blasst_prefill(const void* q, const void* k, const void* v, float* o, float* lse,
+                             uint8_t* skip_mask, int B, int Hq, int T, int d, int gqa_ratio,
+                             int Bc, double lambda, int causal, blasst_stream_t stream);
+
+/*
+ * Split-KV decode step, one query token per (batch, query head).  The KV
+ * blocks [0, ceil(N/Bc)) are cut into num_splits contiguous ranges, split s
+ * covering [floor(s*nk/S), floor((s+1)*nk/S)); each split runs the online
+ * softmax from a fresh state (running max -inf) and writes its normalised
+ * partial output and log-sum-exp (split-KV tiles as in the SANTA notes'
+ * FlashDecoding pattern).  Within a split, the blog's decode kernel is
+ * followed: the S blocks of a batch are formed first, all their decisions
+ * are taken together, and V is loaded only for blocks that some head of the
+ * kv group keeps (section on the decode kernel, batched load scheduling).
+ *
+ *   q          bf16 [B, Hq, 1, d]
+ *   k, v       bf16 [B, Hkv, N, d]       Hkv = Hq / gqa_ratio
+ *   o_part     fp32 [B, Hq, num_splits, d]
+ *   lse_part   fp32 [B, Hq, num_splits]  natural log
+ *   skip_mask  u8   [B, Hq,  ceil(N/Bc)] or NULL   per-head decision
+ *   vskip_mask u8   [B, Hkv, ceil(N/Bc)] or NULL   1 = V block not loaded
+ *   causal     accepted for symmetry; one decode query sees all N keys.
+ *   num_splits 1 <= num_splits <= ceil(N/Bc)
+ * Errors: INVALID_ARG for a null q/k/v/o_part/lse_part, B/Hq < 0, N <= 0,
+ * gqa_ratio < 1 or not dividing Hq, lambda outside [0,1), bad num_splits;
+ * UNSUPPORTED for d or Bc outside {64, 128}, or gqa_ratio > 64.  Scalar
+ * arguments are checked first; then B*Hq == 0 returns OK and does nothing (the
+ * pointers may then be NULL and are not read).
+ */
+blasst_status blasst_decode(const void* q, const void* k, const void* v, float* o_part,
+                            float* lse_part, uint8_t* skip_mask, uint8_t* vskip_mask, int B,
+                            int Hq, int N, int d, int gqa_ratio, int Bc, double lambda,
+                            int causal, int num_splits, blasst_stream_t stream);
+
+/*
+ * Merge of the splits by their true normalisers (SANTA notes, merge of
+ * FlashDecoding tiles): LSE = ln sum_s exp(lse_s), O = sum_s exp(lse_s - LSE) O_s.
+ *
+ *   o_part     fp32 [B, Hq, num_splits, d]
+ *   lse_part   fp32 [B, Hq, num_splits]
+ *   o          fp32 [B, Hq, d]
+ *   lse        fp32 [B, Hq] or NULL
+ * Errors: INVALID_ARG for a null o_part/lse_part/o, B/Hq < 0, num_splits < 1,
+ * d <= 0; UNSUPPORTED for d outside {64, 128}.  B*Hq == 0 returns OK without
+ * reading the pointers.
+ */
+blasst_status blasst_decode_combine(const float* o_part, const float* lse_part, float* o,
+                                    float* lse, int B, int Hq, int d, int num_splits,
+                                    blasst_stream_t stream);
+
+/* Static, human-readable name of a status code. */
+const char* blasst_status_string(blasst_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BLASST_H */

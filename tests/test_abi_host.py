@@ -1,0 +1,91 @@
+"""Host-only checks of the C ABI library: it loads, exports exactly what
+include/blasst.h declares, and rejects bad arguments before touching HIP
+(no GPU is needed for any call made here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "blasst.h")
+LIB = os.path.join(ROOT, "block_sparse_attention_flash_amd", "libblasst.so")
+
+
+def declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(blasst_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        import block_sparse_attention_flash_amd as bsa
+        bsa.build()
+    return ctypes.CDLL(LIB)
+
+
+def test_header_declares_the_entry_points():
+    assert declared() == ["blasst_decode", "blasst_decode_combine", "blasst_prefill", "blasst_status_string"]
+
+
+def test_exports_match_header(lib):
+    for name in declared():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], stdout=subprocess.PIPE, text=True).stdout
+    exported = sorted(set(re.findall(r"\b(blasst_\w+)\b", out)))
+    assert exported == declared()
+
+
+def test_status_strings(lib):
+    lib.blasst_status_string.restype = ctypes.c_char_p
+    names = [lib.blasst_status_string(i).decode() for i in range(5)]
+    assert names[0] == "ok" and len(set(names)) == 5
+    assert lib.blasst_status_string(99).decode() == "unknown status"
+
+
+P = ctypes.c_void_p
+I = ctypes.c_int
+D = ctypes.c_double
+FAKE = P(0x1000)   # 16-byte aligned, never dereferenced: validation fails first
+
+
+def prefill(lib, q=FAKE, o=FAKE, B=1, Hq=4, T=256, d=128, G=4, Bc=128, lam=1e-3, causal=1):
+    f = lib.blasst_prefill
+    f.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, D, I, P]
+    return f(q, FAKE, FAKE, o, None, None, B, Hq, T, d, G, Bc, lam, causal, None)
+
+
+def decode(lib, q=FAKE, B=1, Hq=4, N=256, d=128, G=4, Bc=128, lam=1e-3, S=2, causal=1):
+    f = lib.blasst_decode
+    f.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, D, I, I, P]
+    return f(q, FAKE, FAKE, FAKE, FAKE, None, None, B, Hq, N, d, G, Bc, lam, causal, S, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(o=None), 1), (dict(B=-1), 1), (dict(T=-5), 1), (dict(G=0), 1),
+    (dict(G=3), 1), (dict(lam=1.0), 1), (dict(lam=-1e-3), 1), (dict(lam=float("nan")), 1),
+    (dict(causal=2), 1), (dict(q=P(0x1008)), 1), (dict(d=96), 2), (dict(Bc=32), 2), (dict(d=256), 2),
+    (dict(B=0), 0), (dict(T=0), 0),
+])
+def test_prefill_validation(lib, kw, status):
+    assert prefill(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(N=0), 1), (dict(S=0), 1), (dict(S=3), 1), (dict(G=5), 1),
+    (dict(lam=1.5), 1), (dict(causal=-1), 1), (dict(d=80), 2), (dict(Bc=256, S=1), 2),
+    (dict(Hq=128, G=128), 2), (dict(B=0), 0), (dict(Hq=0), 0),
+])
+def test_decode_validation(lib, kw, status):
+    assert decode(lib, **kw) == status
+
+
+def test_combine_validation(lib):
+    f = lib.blasst_decode_combine
+    f.argtypes = [P, P, P, P, I, I, I, I, P]
+    assert f(None, FAKE, FAKE, None, 1, 4, 128, 2, None) == 1
+    assert f(FAKE, FAKE, FAKE, None, 1, 4, 128, 0, None) == 1
+    assert f(FAKE, FAKE, FAKE, None, 1, 4, 96, 2, None) == 2
+    assert f(FAKE, FAKE, FAKE, None, 0, 4, 128, 2, None) == 0
