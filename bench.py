@@ -104,22 +104,27 @@ def bench_decode(args, lib, torch, W):
         check(combine_fn(*comb))
     torch.cuda.synchronize()
 
-    # timed region: K steps; events bracket every split launch on the launch stream
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # timed region: K steps (split + combine), HIP events on the launch stream at both ends
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record(stream)
     for s in range(args.steps):
-        ev[s][0].record(stream)
         check(decode_fn(*sargs[s % len(sargs)]))
-        ev[s][1].record(stream)
         check(combine_fn(*comb))
     stop.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     step_ms = start.elapsed_time(stop) / args.steps
-    split_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    # the split kernel alone: K back-to-back launches between one pair of events
+    torch.cuda.synchronize()
+    start.record(stream)
+    for s in range(args.steps):
+        check(decode_fn(*sargs[s % len(sargs)]))
+    stop.record(stream)
+    torch.cuda.synchronize()
+    split_ms = start.elapsed_time(stop) / args.steps
 
     # dense-equivalent reference (lambda = 0): same kernels, nothing skipped
     for s in range(args.warmup):

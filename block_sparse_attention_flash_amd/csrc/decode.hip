@@ -5,28 +5,33 @@
 // block max, which needs S = q K^T; deciding block by block would serialise
 // "decide -> load V".  The blog's answer is batched load scheduling: form the
 // S blocks of a batch first, decide them together, then issue V loads only for
-// kept blocks.  That is the structure here.
+// kept blocks.  Here a batch ("phase") is as large as the registers allow
+// (for 4-head groups at Bc = 128: 16 blocks, a whole 32K/16-way split).
 //
-// Work decomposition (one workgroup = 4 waves per (batch b, kv head, split)):
-//  * The split's KV blocks are walked in batches.  Every block is cut into
-//    32-key units; a wave owns NB units per batch.  For Bc = 128 wave w takes
-//    keys [32w, 32w+32) of each of NB consecutive blocks.
-//  * S^T = K q^T for a unit runs on MFMA 16x16x32 bf16 with the 32 keys as two
-//    16-row tiles and the G query heads of the group as the 16-wide column
-//    tiles (NT tiles of 16; heads beyond G are zero columns that never vote).
-//    K fragments are loaded straight from HBM into the MFMA A-operand layout
-//    (16 bytes per lane, each row of 16 lanes a contiguous 64-byte run).
-//  * Each unit's per-head partial max goes through LDS; after one barrier every
-//    lane knows the block maxima of the whole batch.  Because a skipped block
-//    never moves the running max (mt < m + ln(lambda) < m), the running max
-//    before block j is the prefix max of the block maxima, so all decisions of
-//    the batch are taken at once, in block order, with no cascade.
-//  * V rows are loaded only for blocks some head of the group keeps, staged
-//    through a wave-private LDS slot and read back transposed
-//    (ds_read_b64_tr_b16) as the A operand of O^T += V^T P^T.  P^T comes
-//    straight from the S^T accumulators (same lane layout), rounded to bf16.
-//  * Scores are kept in log2 units (t = s * log2(e)), so P = 2^(t - m) uses
-//    v_exp_f32 directly and the test reads t~ - m < ln(lambda) * log2(e).
+// One workgroup = W waves per (batch b, kv head, split).  Each block is cut
+// into 32-key units; wave w owns units w, w+W, w+2W, ... of the phase.
+//
+//  K pass   every unit's K rows go straight from HBM into the MFMA A layout
+//           (16 bytes per lane) through a small register ring, so loads for
+//           later units are in flight while earlier ones are multiplied.
+//           S^T = K q^T runs on MFMA 16x16x32 bf16 with the 32 keys as two
+//           16-row tiles and the G query heads of the group as 16-wide
+//           column tiles (heads beyond G are zero columns that never vote).
+//           The S^T tiles stay in registers; each unit's per-head partial
+//           max goes to LDS.
+//  decide   one barrier; every lane then walks the phase's blocks in order.
+//           Because a skipped block never moves the running max
+//           (mt < m + ln(lambda) < m), the running max before block j is the
+//           prefix max of the block maxima: all decisions of the phase are
+//           taken at once with no cascade.  V is needed for a block iff some
+//           head of the group keeps it.
+//  V pass   only kept units: V rows go HBM -> LDS (global_load_lds_dwordx4,
+//           pre-swizzled addresses) through a two-slot ring per wave, and are
+//           read back transposed (ds_read_b64_tr_b16) as the A operand of
+//           O^T += V^T P^T.  P^T is the S^T accumulator (same lane layout)
+//           after 2^(t - m), rounded to bf16.
+// Scores are kept in log2 units (t = s * log2(e)), so P uses v_exp_f32 directly
+// and the test reads t~ - m < ln(lambda) * log2(e).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -34,24 +39,24 @@ namespace blasst {
 
 namespace {
 
-constexpr int kDecodeThreads = 256;  // 4 waves
-
-template <int D, int BC, int NT, int NB>
-__global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(DecodeArgs a) {
+template <int D, int BC, int NT, int UW, int W, int KR>
+__global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
     constexpr int KG = BC / 32;           // 32-key units per block
-    constexpr int NBB = 4 * NB / KG;      // blocks per batch
+    constexpr int UPP = W * UW;           // units per phase
+    constexpr int BPP = UPP / KG;         // blocks per phase
     constexpr int DS = D / 32;            // MFMA k-steps over d for S
     constexpr int DT = D / 16;            // 16-wide d tiles of O^T
     constexpr int FR = D / 16;            // 16-byte fragments per lane per unit
     constexpr int CPR = D / 8;            // 16-byte chunks per K/V row
     constexpr int HT = 16 * NT;           // head columns per workgroup
-    constexpr int VSLOT = 32 * D * 2;     // bytes of one staged 32-row V slice
-    static_assert(NBB * KG == 4 * NB, "units must tile the batch");
-    static_assert(4 * DT * 4 * 64 * 4 <= 4 * VSLOT, "O reduction must fit the V staging area");
+    constexpr int VSLOT = 32 * D * 2;     // bytes of one 32-row V slice
+    static_assert(UPP % KG == 0, "units must tile the phase");
+    static_assert(BPP <= 32, "decision masks are 32-bit");
+    static_assert(W * DT * 4 * 64 * 4 <= 2 * W * VSLOT, "O reduction must fit the V staging area");
 
-    __shared__ __attribute__((aligned(16))) char lds_v[4 * VSLOT];
-    __shared__ float lds_pmax[2][NBB * KG * HT];
-    __shared__ float lds_l[4][64];
+    __shared__ __attribute__((aligned(16))) char lds_v[2 * W * VSLOT];
+    __shared__ float lds_pmax[2][UPP * HT];
+    __shared__ float lds_l[W][64];
 
     const int split = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -62,7 +67,6 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(DecodeArgs
 
     const uint16_t* kbase = a.k + ((size_t)b * a.Hkv + hkv) * (size_t)N * D;
     const uint16_t* vbase = a.v + ((size_t)b * a.Hkv + hkv) * (size_t)N * D;
-    lds_char* vslot = (lds_char*)(lds_v + wave * VSLOT);
 
     // q^T as the B operand: lane (g, n) holds q[head n][32s + 8g .. +8].
     bf16x8 qf[NT][DS];
@@ -90,37 +94,36 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(DecodeArgs
     }
 
     int parity = 0;
-    for (int jb0 = j0; jb0 < j1; jb0 += NBB, parity ^= 1) {
-        // ---- units of this wave in the batch
-        int ublk[NB], ukey0[NB];
-        bool uok[NB];
+    for (int p0 = j0; p0 < j1; p0 += BPP, parity ^= 1) {
+        const int nb = min(BPP, j1 - p0);
+        int ukey0[UW];
+        bool uok[UW];
 #pragma unroll
-        for (int u = 0; u < NB; ++u) {
-            const int U = wave + 4 * u;
-            ublk[u] = jb0 + U / KG;
-            ukey0[u] = ublk[u] * BC + (U % KG) * 32;
-            uok[u] = ublk[u] < j1;
+        for (int u = 0; u < UW; ++u) {
+            const int U = wave + W * u;
+            ukey0[u] = (p0 + U / KG) * BC + (U % KG) * 32;
+            uok[u] = U / KG < nb;
         }
 
-        // ---- K fragments straight into the MFMA A layout
-        u32x4 kv[NB][FR];
-#pragma unroll
-        for (int u = 0; u < NB; ++u) {
+        // ================= K pass =================
+        u32x4 kr[KR][FR];
+        auto load_k = [&](int slot, int u) {
+            const int U = wave + W * u;
+            const int blk = min(p0 + U / KG, j1 - 1);  // past the split: re-read a cached block
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {
-                const int key = min(ukey0[u] + 16 * kt + n, N - 1);
+                const int key = min(blk * BC + (U % KG) * 32 + 16 * kt + n, N - 1);
 #pragma unroll
-                for (int s = 0; s < DS; ++s) {
-                    if (uok[u]) kv[u][kt * DS + s] = load16(kbase + (size_t)key * D + 32 * s + 8 * g);
-                    else kv[u][kt * DS + s] = u32x4{0u, 0u, 0u, 0u};
-                }
+                for (int s = 0; s < DS; ++s) kr[slot][kt * DS + s] = load16(kbase + (size_t)key * D + 32 * s + 8 * g);
             }
-        }
-
-        // ---- S^T = K q^T, scaled to log2 units, tail keys masked; partial maxima
-        f32x4 t[NB][2][NT];
+        };
 #pragma unroll
-        for (int u = 0; u < NB; ++u) {
+        for (int u = 0; u < (KR < UW ? KR : UW); ++u) load_k(u, u);
+
+        f32x4 t[UW][2][NT];
+#pragma unroll
+        for (int u = 0; u < UW; ++u) {
+            const int slot = u % KR;
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
                 float pm = kNegInf;
@@ -128,7 +131,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(DecodeArgs
                 for (int kt = 0; kt < 2; ++kt) {
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int s = 0; s < DS; ++s) acc = mfma16x16x32(as_bf16x8(kv[u][kt * DS + s]), qf[nt][s], acc);
+                    for (int s = 0; s < DS; ++s) acc = mfma16x16x32(as_bf16x8(kr[slot][kt * DS + s]), qf[nt][s], acc);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int key = ukey0[u] + 16 * kt + 4 * g + i;
@@ -141,13 +144,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(DecodeArgs
                 }
                 pm = fmaxf(pm, wave_shfl_xor(pm, 16));
                 pm = fmaxf(pm, wave_shfl_xor(pm, 32));
-                if (uok[u] && g == 0) lds_pmax[parity][(wave + 4 * u) * HT + nt * 16 + n] = pm;
+                if (uok[u] && g == 0) lds_pmax[parity][(wave + W * u) * HT + nt * 16 + n] = pm;
             }
+            if (u + KR < UW) load_k(slot, u + KR);
         }
         __syncthreads();
 
-        // ---- decisions for the whole batch (prefix max; no cascade)
-        const int nblk = min(NBB, j1 - jb0);
+        // ================= decide (prefix max; no cascade) =================
         uint32_t keep[NT];
         uint32_t vkeep = 0;
         float alpha[NT];
@@ -155,13 +158,15 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(DecodeArgs
         for (int nt = 0; nt < NT; ++nt) {
             float m = m_run[nt];
             uint32_t kb = 0;
-            for (int bi = 0; bi < nblk; ++bi) {
-                float bm = kNegInf;
 #pragma unroll
-                for (int kg = 0; kg < KG; ++kg) bm = fmaxf(bm, lds_pmax[parity][(bi * KG + kg) * HT + nt * 16 + n]);
-                m = fmaxf(m, bm);
-                const bool skip = (bm - m) < a.thr;
-                kb |= (uint32_t)(!skip) << bi;
+            for (int bi = 0; bi < BPP; ++bi) {
+                if (bi < nb) {
+                    float bm = kNegInf;
+#pragma unroll
+                    for (int kg = 0; kg < KG; ++kg) bm = fmaxf(bm, lds_pmax[parity][(bi * KG + kg) * HT + nt * 16 + n]);
+                    m = fmaxf(m, bm);
+                    kb |= (uint32_t)(!((bm - m) < a.thr)) << bi;
+                }
             }
             kb = head_ok[nt] ? kb : 0u;
             keep[nt] = kb;
@@ -174,21 +179,40 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(DecodeArgs
         vkeep |= __shfl_xor(vkeep, 4, 64);
         vkeep |= __shfl_xor(vkeep, 8, 64);
 
-        // ---- decision bytes
-        if (wave == 0 && g == 0) {
+        // decision bytes: one lane per (head, block)
+        if (a.skip != nullptr) {
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
-                if (!head_ok[nt] || a.skip == nullptr) continue;
-                uint8_t* row = a.skip + ((size_t)b * a.Hq + (size_t)hkv * G + nt * 16 + n) * nk + jb0;
-                for (int bi = 0; bi < nblk; ++bi) row[bi] = (uint8_t)(((keep[nt] >> bi) & 1u) ^ 1u);
-            }
-            if (n == 0 && a.vskip != nullptr) {
-                uint8_t* row = a.vskip + ((size_t)b * a.Hkv + hkv) * nk + jb0;
-                for (int bi = 0; bi < nblk; ++bi) row[bi] = (uint8_t)(((vkeep >> bi) & 1u) ^ 1u);
+                const int h = nt * 16 + n;
+                if (!head_ok[nt]) continue;
+                uint8_t* row = a.skip + ((size_t)b * a.Hq + (size_t)hkv * G + h) * nk + p0;
+                for (int bi = wave * 4 + g; bi < nb; bi += 4 * W) row[bi] = (uint8_t)(((keep[nt] >> bi) & 1u) ^ 1u);
             }
         }
+        if (a.vskip != nullptr) {
+            uint8_t* row = a.vskip + ((size_t)b * a.Hkv + hkv) * nk + p0;
+            for (int bi = threadIdx.x; bi < nb; bi += 64 * W) row[bi] = (uint8_t)(((vkeep >> bi) & 1u) ^ 1u);
+        }
 
-        // ---- rescale the running state to the batch's new max
+        // ================= V pass (kept units only) =================
+        bool kept[UW];
+#pragma unroll
+        for (int u = 0; u < UW; ++u) kept[u] = uok[u] && ((vkeep >> ((wave + W * u) / KG)) & 1u);
+
+        auto issue_v = [&](int u) {
+            const char* slot = lds_v + (2 * wave + (u & 1)) * VSLOT;
+#pragma unroll
+            for (int f = 0; f < FR; ++f) {
+                const int p = 64 * f + lane;
+                const int row = p / CPR, cc = (p % CPR) ^ (row & (CPR - 1));
+                const int key = min(ukey0[u] + row, N - 1);
+                global_to_lds16(vbase + (size_t)key * D + cc * 8, lds_addr(slot + 1024 * f));
+            }
+        };
+        if (kept[0]) issue_v(0);
+        if (UW > 1 && kept[UW > 1 ? 1 : 0]) issue_v(1);
+
+        // rescale the running state to the phase's new max (overlaps the V loads)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             l_part[nt] *= alpha[nt];
@@ -196,75 +220,53 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(DecodeArgs
             for (int dt = 0; dt < DT; ++dt) oacc[nt][dt] *= alpha[nt];
         }
 
-        // ---- V loads, kept blocks only (coalesced rows; reuse the K registers)
-        bool uv[NB];
 #pragma unroll
-        for (int u = 0; u < NB; ++u) {
-            uv[u] = uok[u] && ((vkeep >> ((wave + 4 * u) / KG)) & 1u);
-            if (uv[u]) {
+        for (int u = 0; u < UW; ++u) {
+            if (kept[u]) {
+                // V(u) is complete once at most the next unit's loads are outstanding
+                if (u + 1 < UW && kept[u + 1 < UW ? u + 1 : u]) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(FR) : "memory");
+                else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                const lds_char* vslot = (const lds_char*)(lds_v + (2 * wave + (u & 1)) * VSLOT);
+                const int blk_bit = (wave + W * u) / KG;
+                bf16x8 pf[NT];
 #pragma unroll
-                for (int f = 0; f < FR; ++f) {
-                    const int c = lane + 64 * f;
-                    const int key = min(ukey0[u] + c / CPR, N - 1);
-                    kv[u][f] = load16(vbase + (size_t)key * D + (c % CPR) * 8);
+                for (int nt = 0; nt < NT; ++nt) {
+                    const bool kp = (keep[nt] >> blk_bit) & 1u;
+                    float p[8];
+#pragma unroll
+                    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float e = exp2_fast(t[u][kt][nt][i] - m_run[nt]);
+                            p[4 * kt + i] = kp ? e : 0.f;
+                        }
+                    l_part[nt] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+                    u32x4 w4 = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                                pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+                    pf[nt] = as_bf16x8(w4);
                 }
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    const int cc = 2 * dt + ((n & 3) >> 1);
+                    const int r0 = 4 * g + (n >> 2), r1 = 16 + 4 * g + (n >> 2);
+                    const u32x2 lo = lds_read_tr16(vslot + r0 * (2 * D) + ((cc ^ (r0 & (CPR - 1))) << 4) + (n & 1) * 8);
+                    const u32x2 hi = lds_read_tr16(vslot + r1 * (2 * D) + ((cc ^ (r1 & (CPR - 1))) << 4) + (n & 1) * 8);
+                    const bf16x8 av = as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y});
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) oacc[nt][dt] = mfma16x16x32(av, pf[nt], oacc[nt][dt]);
+                }
+            }
+            if (u + 2 < UW && kept[u + 2 < UW ? u + 2 : u]) {
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // slot (u & 1) has been read
+                issue_v(u + 2);
             }
         }
-
-        // ---- P V for kept units: stage V through LDS, read it back transposed
-#pragma unroll
-        for (int u = 0; u < NB; ++u) {
-            if (!uv[u]) continue;
-#pragma unroll
-            for (int f = 0; f < FR; ++f) {
-                const int c = lane + 64 * f;
-                const int row = c / CPR, cc = c % CPR;
-                *(u32x4*)(lds_v + wave * VSLOT + row * (2 * D) + ((cc ^ (row & (CPR - 1))) << 4)) = kv[u][f];
-            }
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-
-            bf16x8 pf[NT];
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const bool kp = (keep[nt] >> ((wave + 4 * u) / KG)) & 1u;
-                float p[8];
-#pragma unroll
-                for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float e = exp2_fast(t[u][kt][nt][i] - m_run[nt]);
-                        p[4 * kt + i] = kp ? e : 0.f;
-                    }
-                float ps = 0.f;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) ps += p[i];
-                l_part[nt] += ps;
-                u32x4 w = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                           pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
-                pf[nt] = as_bf16x8(w);
-            }
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                u32x2 lo, hi;
-                {
-                    const int r = 4 * g + (n >> 2), cc = 2 * dt + ((n & 3) >> 1);
-                    lo = lds_read_tr16(vslot + r * (2 * D) + ((cc ^ (r & (CPR - 1))) << 4) + (n & 1) * 8);
-                }
-                {
-                    const int r = 16 + 4 * g + (n >> 2), cc = 2 * dt + ((n & 3) >> 1);
-                    hi = lds_read_tr16(vslot + r * (2 * D) + ((cc ^ (r & (CPR - 1))) << 4) + (n & 1) * 8);
-                }
-                const bf16x8 av = as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y});
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) oacc[nt][dt] = mfma16x16x32(av, pf[nt], oacc[nt][dt]);
-            }
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
 
-    // ---- reduce the four waves' partial O^T and l; write the split's result
+    // ---- reduce the waves' partial O^T and l; write the split's result
     __syncthreads();
-    float* red = (float*)lds_v;  // [4 waves][DT][4][64]
+    float* red = (float*)lds_v;  // [W waves][DT][4][64]
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         float l = l_part[nt];
@@ -276,18 +278,20 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(DecodeArgs
             for (int i = 0; i < 4; ++i) red[((wave * DT + dt) * 4 + i) * 64 + lane] = oacc[nt][dt][i];
         lds_l[wave][lane] = l;
         __syncthreads();
-        const float lt = lds_l[0][lane] + lds_l[1][lane] + lds_l[2][lane] + lds_l[3][lane];
+        float lt = 0.f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) lt += lds_l[w][lane];
         const int h = nt * 16 + n;
         if (h < G) {
             const size_t orow = ((size_t)b * a.Hq + (size_t)hkv * G + h) * a.S + split;
             const float inv = 1.f / lt;
-            for (int dt = wave; dt < DT; dt += 4) {
+            for (int dt = wave; dt < DT; dt += W) {
                 float o4[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     float x = 0.f;
 #pragma unroll
-                    for (int w = 0; w < 4; ++w) x += red[((w * DT + dt) * 4 + i) * 64 + lane];
+                    for (int w = 0; w < W; ++w) x += red[((w * DT + dt) * 4 + i) * 64 + lane];
                     o4[i] = x * inv;
                 }
                 *(f32x4*)(a.o_part + orow * D + 16 * dt + 4 * g) = f32x4{o4[0], o4[1], o4[2], o4[3]};
@@ -298,37 +302,60 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(DecodeArgs
     }
 }
 
+// Merge of S split results per (b, head) row.  One workgroup per row, one
+// thread per d column.  Up to 32 splits every load is issued at once (one
+// memory round trip); beyond that the splits are walked in a loop.
 template <int D>
 __global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restrict__ o_part,
                                                             const float* __restrict__ lse_part,
                                                             float* __restrict__ o, float* __restrict__ lse,
                                                             int S) {
+    constexpr int SMAX = 32;
     const size_t row = blockIdx.x;
     const int e = threadIdx.x;
     const float* L = lse_part + row * S;
-    float top = kNegInf;
-    for (int s = 0; s < S; ++s) top = fmaxf(top, L[s]);
-    float z = 0.f;
-    for (int s = 0; s < S; ++s) z += exp2_fast((L[s] - top) * kLog2e);
-    const float total = top + logf(z);
-    float acc = 0.f;
-    for (int s = 0; s < S; ++s) acc += exp2_fast((L[s] - total) * kLog2e) * o_part[(row * S + s) * D + e];
+    const float* op = o_part + row * S * D + e;
+    float acc = 0.f, total;
+    if (S <= SMAX) {
+        float lv[SMAX], xv[SMAX];
+#pragma unroll
+        for (int s = 0; s < SMAX; ++s) {
+            lv[s] = s < S ? L[s] : kNegInf;
+            xv[s] = s < S ? op[(size_t)s * D] : 0.f;
+        }
+        float top = kNegInf;
+#pragma unroll
+        for (int s = 0; s < SMAX; ++s) top = fmaxf(top, lv[s]);
+        float z = 0.f;
+#pragma unroll
+        for (int s = 0; s < SMAX; ++s) z += exp2_fast((lv[s] - top) * kLog2e);
+        total = top + logf(z);
+#pragma unroll
+        for (int s = 0; s < SMAX; ++s) acc += exp2_fast((lv[s] - total) * kLog2e) * xv[s];
+    } else {
+        float top = kNegInf;
+        for (int s = 0; s < S; ++s) top = fmaxf(top, L[s]);
+        float z = 0.f;
+        for (int s = 0; s < S; ++s) z += exp2_fast((L[s] - top) * kLog2e);
+        total = top + logf(z);
+        for (int s = 0; s < S; ++s) acc += exp2_fast((L[s] - total) * kLog2e) * op[(size_t)s * D];
+    }
     o[row * D + e] = acc;
     if (e == 0 && lse != nullptr) lse[row] = total;
 }
 
-template <int D, int BC, int NT, int NB>
+template <int D, int BC, int NT, int UW, int W, int KR>
 hipError_t launch_split(const DecodeArgs& a, hipStream_t stream) {
     dim3 grid(a.S, a.Hkv, a.B);
-    hipLaunchKernelGGL((decode_split_kernel<D, BC, NT, NB>), grid, dim3(kDecodeThreads), 0, stream, a);
+    hipLaunchKernelGGL((decode_split_kernel<D, BC, NT, UW, W, KR>), grid, dim3(64 * W), 0, stream, a);
     return hipGetLastError();
 }
 
 template <int D, int BC>
 hipError_t launch_split_nt(const DecodeArgs& a, hipStream_t stream) {
-    if (a.G <= 16) return launch_split<D, BC, 1, 4>(a, stream);
-    if (a.G <= 32) return launch_split<D, BC, 2, 2>(a, stream);
-    return launch_split<D, BC, 4, 2>(a, stream);
+    if (a.G <= 16) return launch_split<D, BC, 1, 8, 8, 2>(a, stream);
+    if (a.G <= 32) return launch_split<D, BC, 2, 4, 8, 2>(a, stream);
+    return launch_split<D, BC, 4, 2, 4, 2>(a, stream);
 }
 
 }  // namespace

@@ -63,6 +63,20 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const lds_char* p) {
     return __builtin_bit_cast(u32x2, r);
 }
 
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const lds_char*)p;
+}
+
+// 16-byte HBM -> LDS copy (global_load_lds_dwordx4): lane l's 16 bytes land at
+// lds_base + 16*l, lds_base being wave-uniform (it travels in M0).  Issued as
+// inline asm so the compiler adds no wait of its own for the LDS bytes it cannot
+// see; the caller waits with an explicit, counted s_waitcnt vmcnt.
+__device__ __forceinline__ void global_to_lds16(const void* gptr, uint32_t lds_base) {
+    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(__builtin_amdgcn_readfirstlane(lds_base))
+                 : "memory");
+}
+
 __device__ __forceinline__ float wave_shfl_xor(float x, int mask) {
     return __shfl_xor(x, mask, 64);
 }
