@@ -44,7 +44,61 @@ def parse():
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--profile-target", choices=["decode", "prefill", "copy"], default=None,
+                   help="run only one kernel a few times (for hardware-counter collection) and exit")
+    p.add_argument("--profile-launches", type=int, default=10)
     return p.parse_args()
+
+
+COPY_BYTES = 512 << 20  # plain device-to-device copy used to calibrate byte counters
+
+
+def profile_target(args, lib, torch, W):
+    """Launch one kernel --profile-launches times on the bench workload (no timing, no JSON)."""
+    n = args.profile_launches
+    if args.profile_target == "copy":
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(n):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print("copy: %d launches of %d bytes read + %d bytes written" % (n, COPY_BYTES, COPY_BYTES))
+        return
+    if args.profile_target == "decode":
+        w = W.CONFIGS["decode_32k"]
+        copies = [{k: dev(v) for k, v in W.generate(w).items()} for _ in range(max(1, args.copies))]
+        B, Hq, N, d, Bc, S = w.B, w.Hq, w.T, w.d, w.Bc, w.num_splits
+        nk = -(-N // Bc)
+        o_part = torch.empty((B, Hq, S, d), dtype=torch.float32, device="cuda")
+        lse_part = torch.empty((B, Hq, S), dtype=torch.float32, device="cuda")
+        skip = torch.empty((B, Hq, nk), dtype=torch.uint8, device="cuda")
+        vskip = torch.empty((B, w.Hkv, nk), dtype=torch.uint8, device="cuda")
+        sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+        for i in range(n):
+            c = copies[i % len(copies)]
+            assert lib.blasst_decode(P(c["q"]), P(c["k"]), P(c["v"]), P(o_part), P(lse_part), P(skip), P(vskip),
+                                     B, Hq, N, d, w.G, Bc, ctypes.c_double(w.lambdas[0]), 1, S, sp) == 0
+        torch.cuda.synchronize()
+        by = decode_bytes(w, vskip.cpu().numpy())
+        print("decode_32k: %d launches, algorithmic bytes per launch %d (read %d, written %d)" % (
+            n, by["split"], by["k"] + by["v_kept"] + B * Hq * d * 2,
+            by["split"] - by["k"] - by["v_kept"] - B * Hq * d * 2))
+        return
+    w = W.CONFIGS["prefill_32k"]
+    x = {k: dev(v) for k, v in W.generate(w).items()}
+    B, Hq, T, d, Bc = w.B, w.Hq, w.T, w.d, w.Bc
+    nq = -(-T // Bc)
+    o = torch.empty((B, Hq, T, d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device="cuda")
+    mask = torch.empty((B, Hq, nq, nq), dtype=torch.uint8, device="cuda")
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    for _ in range(n):
+        assert lib.blasst_prefill(P(x["q"]), P(x["k"]), P(x["v"]), P(o), P(lse), P(mask), B, Hq, T, d, w.G, Bc,
+                                  ctypes.c_double(1e-3), 1, sp) == 0
+    torch.cuda.synchronize()
+    print("prefill_32k: %d launches at lambda=1e-3" % n)
 
 
 def dev(bits):
@@ -221,6 +275,9 @@ def main():
     import workloads as W
     torch.cuda.set_device(0)
     lib = bsa._load()
+    if args.profile_target:
+        profile_target(args, lib, torch, W)
+        return
 
     d = bench_decode(args, lib, torch, W)
     pre = None if args.no_prefill else bench_prefill(args, lib, torch, W)

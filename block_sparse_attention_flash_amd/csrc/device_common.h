@@ -63,6 +63,32 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const lds_char* p) {
     return __builtin_bit_cast(u32x2, r);
 }
 
+// Two transposed 8-byte reads joined into one 8 x bf16 MFMA operand (the
+// shuffle lets the two results land in one register quad, with no moves).
+__device__ __forceinline__ bf16x8 lds_read_tr16_pair(const lds_char* lo, const lds_char* hi) {
+    const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)lo);
+    const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)hi);
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    const i16x8 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, ab);
+}
+
+// XOR mask applied to the 16-byte chunk index of row r of a K/V tile in LDS.
+// With 16 chunks per row (256-byte rows) it is the GF(2)-linear map sending the
+// row's bits 0..3 to 4, 10, 1, 2; with 8 chunks per row, bits 0..2 to 2, 4, 1.
+// An exhaustive search over such maps found these conflict-free (256-byte
+// rows) or least-conflicting (128-byte rows) for both access patterns used on
+// the tiles -- 32 consecutive rows x one chunk (ds_read_b128, MFMA A rows) and
+// 4 consecutive rows x two chunks per 16 lanes (ds_read_b64_tr_b16) -- whether
+// the LDS serves 32 or 64 banks per cycle.
+template <int CPR>
+__device__ __forceinline__ int chunk_swizzle(int r) {
+    if constexpr (CPR == 16)
+        return ((r & 1) * 4) ^ (((r >> 1) & 1) * 10) ^ ((r >> 2) & 1) ^ (((r >> 3) & 1) * 2);
+    else
+        return ((r & 1) * 2) ^ (((r >> 1) & 1) * 4) ^ ((r >> 2) & 1);
+}
+
 // LDS byte address of a pointer into a __shared__ array.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const lds_char*)p;

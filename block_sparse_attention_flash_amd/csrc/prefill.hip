@@ -93,19 +93,40 @@ __global__ __launch_bounds__(2 * BC * HPW) void prefill_kernel(PrefillArgs a) {
     float m = kNegInf, l = 0.f;  // m in raw (unscaled) score units
 
     // ---- tile copy: this wave's 1 KiB pieces, LDS position p -> row p / CPR,
-    //      physical chunk p % CPR holding logical chunk (p % CPR) ^ (row % CPR)
+    //      physical chunk p % CPR holding logical chunk (p % CPR) ^ swizzle(row)
     auto issue_tile = [&](int j, int stage) {
 #pragma unroll
         for (int f = 0; f < CPW; ++f) {
             const int piece = wave * CPW + f;
             const int p = piece * 64 + lane;
-            const int row = p / CPR, cc = (p % CPR) ^ (row & (CPR - 1));
+            const int row = p / CPR, cc = (p % CPR) ^ chunk_swizzle<CPR>(row);
             const size_t off = (size_t)min(j * BC + row, T - 1) * D + cc * 8;
             global_to_lds16(kbase + off, lds_addr(&lds_k[stage][piece * 1024]));
             global_to_lds16(vbase + off, lds_addr(&lds_v[stage][piece * 1024]));
         }
     };
-    auto swz = [](int row, int chunk) { return row * ROWB + ((chunk ^ (row & (CPR - 1))) << 4); };
+    // Per-lane byte offsets inside a tile.  The swizzle depends on row & 15 only,
+    // which is the same for every 32-key sub-tile, so sub-tile and stage offsets
+    // are compile-time constants added to these.
+    //   K (S^T A operand): row 32kt + col, chunk 2s + half
+    //   V (transposed, PV A operand): row 32kt + 16p + 4(g16 >> 1) + (jj >> 2) (+ 8 for
+    //   the second half), chunk 4dt + 2(g16 & 1) + ((jj & 3) >> 1), 8-byte half (jj & 1)
+    int koff[DS];
+#pragma unroll
+    for (int s = 0; s < DS; ++s) koff[s] = col * ROWB + (((2 * s + half) ^ chunk_swizzle<CPR>(col)) << 4);
+    int voff[2][DT];
+    {
+        const int g16 = lane >> 4, jj = lane & 15;
+#pragma unroll
+        for (int h8 = 0; h8 < 2; ++h8) {
+            const int r = 4 * (g16 >> 1) + (jj >> 2) + 8 * h8;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const int chunk = 4 * dt + 2 * (g16 & 1) + ((jj & 3) >> 1);
+                voff[h8][dt] = r * ROWB + ((chunk ^ chunk_swizzle<CPR>(r)) << 4) + (jj & 1) * 8;
+            }
+        }
+    }
 
     uint8_t* mask_row = a.mask ? a.mask + (((size_t)b * a.Hq + hq) * a.nq + i) * a.nk : nullptr;
 
@@ -123,7 +144,7 @@ __global__ __launch_bounds__(2 * BC * HPW) void prefill_kernel(PrefillArgs a) {
             sacc[kt] = f32x16{};
 #pragma unroll
             for (int s = 0; s < DS; ++s) {
-                const u32x4 kf = *(const u32x4*)(&lds_k[st][swz(32 * kt + col, 2 * s + half)]);
+                const u32x4 kf = *(const u32x4*)(&lds_k[st][32 * kt * ROWB + koff[s]]);
                 sacc[kt] = mfma32x32x16(as_bf16x8(kf), qf[s], sacc[kt]);
             }
         }
@@ -180,15 +201,12 @@ __global__ __launch_bounds__(2 * BC * HPW) void prefill_kernel(PrefillArgs a) {
                 const bf16x8 pb = as_bf16x8(u32x4{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
                                                   pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])});
                 // keys of these 8 slots: 32kt + 16p + 4*half + {0..3} and the same + 8
-                const int g16 = lane >> 4, jj = lane & 15;
-                const int r0 = 32 * kt + 16 * p + 4 * (g16 >> 1) + (jj >> 2);
+                const char* vsub = &lds_v[st][(32 * kt + 16 * p) * ROWB];
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt) {
-                    const int chunk = 4 * dt + 2 * (g16 & 1) + ((jj & 3) >> 1);
-                    const int byte = (jj & 1) * 8;
-                    const u32x2 lo = lds_read_tr16((const lds_char*)(&lds_v[st][swz(r0, chunk) + byte]));
-                    const u32x2 hi = lds_read_tr16((const lds_char*)(&lds_v[st][swz(r0 + 8, chunk) + byte]));
-                    oacc[dt] = mfma32x32x16(as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y}), pb, oacc[dt]);
+                    const bf16x8 av = lds_read_tr16_pair((const lds_char*)(vsub + voff[0][dt]),
+                                                         (const lds_char*)(vsub + voff[1][dt]));
+                    oacc[dt] = mfma32x32x16(av, pb, oacc[dt]);
                 }
             }
         }
