@@ -82,7 +82,7 @@ __device__ __forceinline__ bf16x8 lds_read_tr16_pair(const lds_char* lo, const l
 // 4 consecutive rows x two chunks per 16 lanes (ds_read_b64_tr_b16) -- whether
 // the LDS serves 32 or 64 banks per cycle.
 template <int CPR>
-__device__ __forceinline__ int chunk_swizzle(int r) {
+__device__ __forceinline__ constexpr int chunk_swizzle(int r) {
     if constexpr (CPR == 16)
         return ((r & 1) * 4) ^ (((r >> 1) & 1) * 10) ^ ((r >> 2) & 1) ^ (((r >> 3) & 1) * 2);
     else
@@ -100,6 +100,14 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // see; the caller waits with an explicit, counted s_waitcnt vmcnt.
 __device__ __forceinline__ void global_to_lds16(const void* gptr, uint32_t lds_base) {
     asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(__builtin_amdgcn_readfirstlane(lds_base))
+                 : "memory");
+}
+
+// Same copy with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane byte
+// offset (the instruction's saddr form): one VGPR of address per lane.
+__device__ __forceinline__ void global_to_lds16_sbase(const void* sbase, uint32_t voff, uint32_t lds_base) {
+    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+                 "{m0}"(__builtin_amdgcn_readfirstlane(lds_base))
                  : "memory");
 }
 

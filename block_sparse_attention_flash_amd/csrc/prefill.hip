@@ -64,7 +64,8 @@ __global__ __launch_bounds__(2 * BC * HPW) void prefill_kernel(PrefillArgs a) {
     const int hgrp = bh % hg_count, b = bh / hg_count;
     const int T = a.T;
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int hsub = wave / NWH, wrow = wave % NWH;
     const int hq = hgrp * HPW + hsub;
     const int hkv = hq / a.G;
@@ -92,72 +93,82 @@ __global__ __launch_bounds__(2 * BC * HPW) void prefill_kernel(PrefillArgs a) {
     for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
     float m = kNegInf, l = 0.f;  // m in raw (unscaled) score units
 
-    // ---- tile copy: this wave's 1 KiB pieces, LDS position p -> row p / CPR,
-    //      physical chunk p % CPR holding logical chunk (p % CPR) ^ swizzle(row)
-    auto issue_tile = [&](int j, int stage) {
+    // ---- tile copies: this wave's 1 KiB pieces, LDS position pp -> row pp / CPR,
+    //      physical chunk pp % CPR holding logical chunk (pp % CPR) ^ swizzle(row).
+    //      The byte offset inside a tile is fixed per lane; the tile base is
+    //      wave-uniform.  Only a ragged last tile clamps its rows to T - 1.
+    uint32_t toff[CPW];
+#pragma unroll
+    for (int f = 0; f < CPW; ++f) {
+        const int pp = (wave * CPW + f) * 64 + lane;
+        toff[f] = (uint32_t)((pp / CPR) * ROWB + (((pp % CPR) ^ chunk_swizzle<CPR>(pp / CPR)) << 4));
+    }
+    auto issue = [&](const uint16_t* base, char* lds_tile, int j) {
+        const uint16_t* tbase = base + (size_t)j * BC * D;
+        const bool ragged = (j + 1) * BC > T;
 #pragma unroll
         for (int f = 0; f < CPW; ++f) {
-            const int piece = wave * CPW + f;
-            const int p = piece * 64 + lane;
-            const int row = p / CPR, cc = (p % CPR) ^ chunk_swizzle<CPR>(row);
-            const size_t off = (size_t)min(j * BC + row, T - 1) * D + cc * 8;
-            global_to_lds16(kbase + off, lds_addr(&lds_k[stage][piece * 1024]));
-            global_to_lds16(vbase + off, lds_addr(&lds_v[stage][piece * 1024]));
+            uint32_t off = toff[f];
+            if (ragged) off -= (uint32_t)(max(j * BC + (int)(off / ROWB) - (T - 1), 0) * ROWB);
+            global_to_lds16_sbase(tbase, off, lds_addr(lds_tile + (wave * CPW + f) * 1024));
         }
     };
+    auto issue_k = [&](int j, int stage) { issue(kbase, &lds_k[stage][0], j); };
+    auto issue_v = [&](int j, int stage) { issue(vbase, &lds_v[stage][0], j); };
     // Per-lane byte offsets inside a tile.  The swizzle depends on row & 15 only,
     // which is the same for every 32-key sub-tile, so sub-tile and stage offsets
     // are compile-time constants added to these.
-    //   K (S^T A operand): row 32kt + col, chunk 2s + half
-    //   V (transposed, PV A operand): row 32kt + 16p + 4(g16 >> 1) + (jj >> 2) (+ 8 for
-    //   the second half), chunk 4dt + 2(g16 & 1) + ((jj & 3) >> 1), 8-byte half (jj & 1)
-    int koff[DS];
-#pragma unroll
-    for (int s = 0; s < DS; ++s) koff[s] = col * ROWB + (((2 * s + half) ^ chunk_swizzle<CPR>(col)) << 4);
-    int voff[2][DT];
+    //   K (S^T A operand): row 32kt + col, chunk 2s + half.  2s only touches
+    //   chunk bits 1..3, so the offset for step s is kofs ^ (32 s).
+    //   V (transposed, PV A operand): row 16p + r (+ 8 for the second half) with
+    //   r = 4(g16 >> 1) + (jj >> 2), chunk 4dt + 2(g16 & 1) + ((jj & 3) >> 1),
+    //   8-byte half (jj & 1).  4dt only touches chunk bits 2..3, so dt gives
+    //   vofs ^ (64 dt).  Row r + 8 flips swizzle bit 1 with 16 chunks per row
+    //   (+ 8 rows and ^ 32) and leaves the 8-chunk swizzle unchanged (+ 8 rows).
+    const int kofs = col * ROWB + ((half ^ chunk_swizzle<CPR>(col)) << 4);
+    int vofs;
     {
         const int g16 = lane >> 4, jj = lane & 15;
-#pragma unroll
-        for (int h8 = 0; h8 < 2; ++h8) {
-            const int r = 4 * (g16 >> 1) + (jj >> 2) + 8 * h8;
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const int chunk = 4 * dt + 2 * (g16 & 1) + ((jj & 3) >> 1);
-                voff[h8][dt] = r * ROWB + ((chunk ^ chunk_swizzle<CPR>(r)) << 4) + (jj & 1) * 8;
-            }
-        }
+        const int r = 4 * (g16 >> 1) + (jj >> 2);
+        const int chunk = 2 * (g16 & 1) + ((jj & 3) >> 1);
+        vofs = r * ROWB + ((chunk ^ chunk_swizzle<CPR>(r)) << 4) + (jj & 1) * 8;
     }
+    static_assert(CPR == 8 || CPR == 16, "swizzle offsets assume 8 or 16 chunks per row");
+    constexpr int VH8 = (chunk_swizzle<CPR>(8) ^ chunk_swizzle<CPR>(0)) << 4;
 
     uint8_t* mask_row = a.mask ? a.mask + (((size_t)b * a.Hq + hq) * a.nq + i) * a.nk : nullptr;
 
-    issue_tile(0, 0);
-    for (int j = 0; j < jend; ++j) {
-        const int st = j & 1;
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's pieces of tile j
-        __syncthreads();                                   // every piece of tile j; stage st^1 free
-        if (j + 1 < jend) issue_tile(j + 1, st ^ 1);
-
-        // ---- S^T = K Q^T for this wave's 32 query columns, all BC keys
-        f32x16 sacc[KT];
+    // ---- phase X_j: S^T(j) = K(j) Q^T, row max, this wave's vote (state kept for Y_j)
+    f32x16 sacc[KT];
+    float m_new = kNegInf;
+    auto phase_x = [&](int j) {
+        const char* kt_base = &lds_k[j & 1][0];
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) {
             sacc[kt] = f32x16{};
 #pragma unroll
             for (int s = 0; s < DS; ++s) {
-                const u32x4 kf = *(const u32x4*)(&lds_k[st][32 * kt * ROWB + koff[s]]);
+                const u32x4 kf = *(const u32x4*)(kt_base + 32 * kt * ROWB + (kofs ^ (32 * s)));
                 sacc[kt] = mfma32x32x16(as_bf16x8(kf), qf[s], sacc[kt]);
             }
         }
-
-        // ---- causal / tail mask (diagonal or ragged tile only), row max over the tile
+        // causal / tail mask (diagonal or ragged tile only)
         const bool need_mask = (a.causal && j == i) || (j + 1) * BC > T;
         if (need_mask) {
+            // key j*BC + 4*half + o is allowed iff o <= lim; branch-free select
+            // (sign of lim - o as a bit mask) keeps the compares out of SGPRs
+            const int lim = min(T - 1, a.causal ? qidx : T - 1) - j * BC - 4 * half;
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                    const int kidx = j * BC + 32 * kt + 8 * (e >> 2) + 4 * half + (e & 3);
-                    if (kidx >= T || (a.causal && kidx > qidx)) sacc[kt][e] = kNegInf;
+                    const int o = 32 * kt + 8 * (e >> 2) + (e & 3);
+                    const uint32_t drop = (uint32_t)((lim - o) >> 31);
+                    // read the element into a scalar first: bit_cast of a vector
+                    // element lvalue reads element 0 with this compiler
+                    const float sv = sacc[kt][e];
+                    const uint32_t sb = __float_as_uint(sv);
+                    sacc[kt][e] = __uint_as_float((sb & ~drop) | (0xff800000u & drop));
                 }
         }
         float mt = kNegInf;
@@ -166,21 +177,21 @@ __global__ __launch_bounds__(2 * BC * HPW) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) mt = fmaxf(mt, sacc[kt][e]);
         mt = fmaxf(mt, wave_shfl_xor(mt, 32));
-
-        // ---- Eq. 1 then the log-space test; AND over every row of the head's query block
-        const float m_new = fmaxf(m, mt);
+        // Eq. 1 then the log-space test (log2 units)
+        m_new = fmaxf(m, mt);
         const bool vote_skip = !row_ok || mt == kNegInf || (mt - m_new) * c < a.thr;
         const bool wave_skip = __all(vote_skip);
         if (lane == 0) lds_vote[wave] = wave_skip;
-        __syncthreads();
+    };
+
+    // ---- phase Y_j: AND over the head's waves; kept tile -> rescale, P, row sum, O^T += V^T P^T
+    auto phase_y = [&](int j) {
         bool skip = true;
 #pragma unroll
         for (int w = 0; w < NWH; ++w) skip = skip && lds_vote[hsub * NWH + w];
         if (wrow == 0 && lane == 0 && mask_row) mask_row[j] = (uint8_t)skip;
-        if (skip) continue;
-
-        // ---- kept tile: rescale (only if some row's max moved), P, row sum, O^T += V^T P^T
-        if (!__all(m_new == m)) {
+        if (skip) return;
+        if (!__all(m_new == m)) {  // rescale only when some row's max moved
             const float alpha = exp2_fast((m - m_new) * c);
             l *= alpha;
 #pragma unroll
@@ -188,6 +199,7 @@ __global__ __launch_bounds__(2 * BC * HPW) void prefill_kernel(PrefillArgs a) {
         }
         m = m_new;
         const float mc = m * c;
+        const char* vt_base = &lds_v[j & 1][0];
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
@@ -201,17 +213,63 @@ __global__ __launch_bounds__(2 * BC * HPW) void prefill_kernel(PrefillArgs a) {
                 const bf16x8 pb = as_bf16x8(u32x4{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
                                                   pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])});
                 // keys of these 8 slots: 32kt + 16p + 4*half + {0..3} and the same + 8
-                const char* vsub = &lds_v[st][(32 * kt + 16 * p) * ROWB];
+                const char* vsub = vt_base + (32 * kt + 16 * p) * ROWB;
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt) {
-                    const bf16x8 av = lds_read_tr16_pair((const lds_char*)(vsub + voff[0][dt]),
-                                                         (const lds_char*)(vsub + voff[1][dt]));
+                    const int vo = vofs ^ (64 * dt);
+                    const bf16x8 av = lds_read_tr16_pair((const lds_char*)(vsub + vo),
+                                                         (const lds_char*)(vsub + 8 * ROWB + (vo ^ VH8)));
                     oacc[dt] = mfma32x32x16(av, pb, oacc[dt]);
                 }
             }
         }
+    };
+
+    // ---- phase schedule.  Head group g runs phase q = p - g of its own sequence
+    //      X_0, Y_0, X_1, Y_1, ...: with two groups, in every phase one group forms
+    //      S (MFMA-heavy) while the other does softmax + P V (VALU-heavy), and each
+    //      SIMD holds one wave of each.  K(j) is read in phases 2j and 2j+1, V(j) in
+    //      2j+1 and 2j+2; both are double-buffered.  Every wave issues its pieces of
+    //      one tile copy per phase (K(p/2 + 1) in even phases, V((p+1)/2) in odd
+    //      ones) into the buffer freed by the previous barrier, and the barrier
+    //      closing the phase waits for every copy but the one just issued.  Each
+    //      group runs its own straight-line loop; both pass the same barriers.
+    auto open_phase = [&](int p) -> bool {
+        const int jn = (p & 1) ? (p + 1) / 2 : p / 2 + 1;
+        if (jn >= jend) return false;
+        if (p & 1) issue_v(jn, jn & 1);
+        else issue_k(jn, jn & 1);
+        return true;
+    };
+    auto close_phase = [&](bool issued) {
+        if (issued) asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(CPW) : "memory");
+        else asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    };
+    issue_k(0, 0);
+    issue_v(0, 0);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CPW) : "memory");  // K(0)
+    __syncthreads();
+    if (HPW == 1 || hsub == 0) {
+        for (int j = 0; j < jend; ++j) {
+            bool is = open_phase(2 * j);
+            phase_x(j);
+            close_phase(is);
+            is = open_phase(2 * j + 1);
+            phase_y(j);
+            close_phase(is);
+        }
+        if (HPW == 2) close_phase(open_phase(2 * jend));
+    } else {
+        close_phase(open_phase(0));
+        for (int j = 0; j < jend; ++j) {
+            bool is = open_phase(2 * j + 1);
+            phase_x(j);
+            close_phase(is);
+            is = open_phase(2 * j + 2);
+            phase_y(j);
+            close_phase(is);
+        }
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // ---- epilogue: O / l and LSE for this lane's row
     l += wave_shfl_xor(l, 32);
