@@ -24,6 +24,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -105,9 +107,14 @@ __device__ __forceinline__ void global_to_lds16(const void* gptr, uint32_t lds_b
 
 // Same copy with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane byte
 // offset (the instruction's saddr form): one VGPR of address per lane.
+// The base must be the same in every lane; readfirstlane states that to the
+// compiler (it cannot always prove it) so the operand is an SGPR pair.
 __device__ __forceinline__ void global_to_lds16_sbase(const void* sbase, uint32_t voff, uint32_t lds_base) {
-    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
-                 "{m0}"(__builtin_amdgcn_readfirstlane(lds_base))
+    const uint64_t p = (uint64_t)sbase;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)p);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+    const void* sp = (const void*)(((uint64_t)hi << 32) | lo);
+    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sp), "{m0}"(__builtin_amdgcn_readfirstlane(lds_base))
                  : "memory");
 }
 

@@ -37,6 +37,15 @@ namespace blasst {
 
 namespace {
 
+#ifndef BLASST_PREFILL_PRIO_Y
+#define BLASST_PREFILL_PRIO_Y 1
+#endif
+constexpr int PRIO_Y = BLASST_PREFILL_PRIO_Y;
+#ifndef BLASST_PREFILL_PFV
+#define BLASST_PREFILL_PFV 2
+#endif
+constexpr int PFV = BLASST_PREFILL_PFV;  // V^T prefetch distance in 16-key sub-tiles
+
 template <int D, int BC, int HPW>
 __global__ __launch_bounds__(2 * BC * HPW) void prefill_kernel(PrefillArgs a) {
     constexpr int NWH = BC / 32;           // waves per head
@@ -143,14 +152,30 @@ __global__ __launch_bounds__(2 * BC * HPW) void prefill_kernel(PrefillArgs a) {
     float m_new = kNegInf;
     auto phase_x = [&](int j) {
         const char* kt_base = &lds_k[j & 1][0];
+        // K fragments n = d-step-major (s = n / KT, kt = n % KT), so consecutive
+        // MFMAs feed the KT independent accumulators; PFK reads kept in flight
+        // ahead of the MFMA that consumes them (LDS latency >> one MFMA)
+        constexpr int NF = KT * DS, PFK = 8;
+        auto kread = [&](int n) -> u32x4 {
+            return *(const u32x4*)(kt_base + 32 * (n % KT) * ROWB + (kofs ^ (32 * (n / KT))));
+        };
+        u32x4 kf[PFK];
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
-            sacc[kt] = f32x16{};
+        for (int n = 0; n < PFK; ++n) kf[n] = kread(n);
 #pragma unroll
-            for (int s = 0; s < DS; ++s) {
-                const u32x4 kf = *(const u32x4*)(kt_base + 32 * kt * ROWB + (kofs ^ (32 * s)));
-                sacc[kt] = mfma32x32x16(as_bf16x8(kf), qf[s], sacc[kt]);
-            }
+        for (int kt = 0; kt < KT; ++kt) sacc[kt] = f32x16{};
+#pragma unroll
+        for (int n = 0; n < NF; ++n) {
+            const u32x4 cur = kf[n % PFK];
+            if (n + PFK < NF) kf[n % PFK] = kread(n + PFK);
+            sacc[n % KT] = mfma32x32x16(as_bf16x8(cur), qf[n / KT], sacc[n % KT]);
+        }
+        // order: PFK reads, then (MFMA n, read n + PFK) pairs, then the last MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, PFK, 0);
+#pragma unroll
+        for (int n = 0; n < NF; ++n) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (n + PFK < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
         // causal / tail mask (diagonal or ragged tile only)
         const bool need_mask = (a.causal && j == i) || (j + 1) * BC > T;
@@ -200,26 +225,48 @@ __global__ __launch_bounds__(2 * BC * HPW) void prefill_kernel(PrefillArgs a) {
         m = m_new;
         const float mc = m * c;
         const char* vt_base = &lds_v[j & 1][0];
+        // Software-pipelined over the 2*KT sub-tiles of 16 keys: P of sub-tile
+        // u + 1 (exp, row sum, bf16 pack) is formed between the four PV MFMAs of
+        // sub-tile u, so this wave keeps the VALU busy while its MFMAs run.
+        auto make_p = [&](int u) -> bf16x8 {
+            float pv[8];
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
+            for (int e = 0; e < 8; ++e) {
+                pv[e] = exp2_fast(__builtin_fmaf(sacc[u >> 1][8 * (u & 1) + e], c, -mc));
+                l += pv[e];
+            }
+            return as_bf16x8(u32x4{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
+                                   pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])});
+        };
+        auto vread = [&](int u, bf16x8* av) {
+            // keys of sub-tile u's 8 slots: 16u + 4*half + {0..3} and the same + 8
+            const char* vsub = vt_base + 16 * u * ROWB;
 #pragma unroll
-            for (int p = 0; p < 2; ++p) {
-                float pv[8];
+            for (int dt = 0; dt < DT; ++dt) {
+                const int vo = vofs ^ (64 * dt);
+                av[dt] = lds_read_tr16_pair((const lds_char*)(vsub + vo), (const lds_char*)(vsub + 8 * ROWB + (vo ^ VH8)));
+            }
+        };
+        // V^T fragments of sub-tile u + PFV are read before the MFMAs of u
+        constexpr int NU = 2 * KT, NB = PFV + 1;
+        bf16x8 av[NB][DT];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    pv[e] = exp2_fast(__builtin_fmaf(sacc[kt][8 * p + e], c, -mc));
-                    l += pv[e];
-                }
-                const bf16x8 pb = as_bf16x8(u32x4{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
-                                                  pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])});
-                // keys of these 8 slots: 32kt + 16p + 4*half + {0..3} and the same + 8
-                const char* vsub = vt_base + (32 * kt + 16 * p) * ROWB;
+        for (int u = 0; u < PFV; ++u) vread(u, av[u]);
+        bf16x8 pb = make_p(0);
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            if (u + PFV < NU) vread(u + PFV, av[(u + PFV) % NB]);
+            const bf16x8 pcur = pb;
+            if (u + 1 < NU) pb = make_p(u + 1);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) oacc[dt] = mfma32x32x16(av[u % NB][dt], pcur, oacc[dt]);
+            if (u + 1 < NU) {
+                if (u + PFV < NU) __builtin_amdgcn_sched_group_barrier(0x100, 2 * DT, 0);  // V^T reads first
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt) {
-                    const int vo = vofs ^ (64 * dt);
-                    const bf16x8 av = lds_read_tr16_pair((const lds_char*)(vsub + vo),
-                                                         (const lds_char*)(vsub + 8 * ROWB + (vo ^ VH8)));
-                    oacc[dt] = mfma32x32x16(av, pb, oacc[dt]);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x400, 2, 0);  // two exp
+                    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // fma, add, pack
                 }
             }
         }
@@ -245,6 +292,11 @@ __global__ __launch_bounds__(2 * BC * HPW) void prefill_kernel(PrefillArgs a) {
         if (issued) asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(CPW) : "memory");
         else asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     };
+    // The wave in phase Y gets the higher issue priority: its PV MFMAs then take
+    // the matrix unit as soon as they are ready (between the S MFMAs of the wave
+    // in phase X) instead of stalling its in-order VALU stream behind them.
+    auto raise_prio = [&] { if (HPW == 2) __builtin_amdgcn_s_setprio(PRIO_Y); };
+    auto lower_prio = [&] { if (HPW == 2) __builtin_amdgcn_s_setprio(0); };
     issue_k(0, 0);
     issue_v(0, 0);
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CPW) : "memory");  // K(0)
@@ -255,7 +307,9 @@ __global__ __launch_bounds__(2 * BC * HPW) void prefill_kernel(PrefillArgs a) {
             phase_x(j);
             close_phase(is);
             is = open_phase(2 * j + 1);
+            raise_prio();
             phase_y(j);
+            lower_prio();
             close_phase(is);
         }
         if (HPW == 2) close_phase(open_phase(2 * jend));
@@ -266,7 +320,9 @@ __global__ __launch_bounds__(2 * BC * HPW) void prefill_kernel(PrefillArgs a) {
             phase_x(j);
             close_phase(is);
             is = open_phase(2 * j + 2);
+            raise_prio();
             phase_y(j);
+            lower_prio();
             close_phase(is);
         }
     }
