@@ -106,24 +106,44 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
         }
 
         // ================= K pass =================
-        u32x4 kr[KR][FR];
-        auto load_k = [&](int slot, int u) {
+        // Each unit's 32 K rows go HBM -> LDS (global_load_lds_dwordx4, whole
+        // rows per instruction, XOR-swizzled by 16-byte chunk) into this wave's
+        // two staging slots -- the same slots and copy pattern as the V pass --
+        // and are read back in the MFMA A layout (ds_read_b128).  Units past
+        // the split re-read its last block (cached), so the wait counts are fixed.
+        auto slot_of = [&](int u) { return lds_v + (2 * wave + (u & 1)) * VSLOT; };
+        auto issue_k = [&](int u) {
             const int U = wave + W * u;
-            const int blk = min(p0 + U / KG, j1 - 1);  // past the split: re-read a cached block
+            const int key0 = min(p0 + U / KG, j1 - 1) * BC + (U % KG) * 32;
+            const char* slot = slot_of(u);
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-                const int key = min(blk * BC + (U % KG) * 32 + 16 * kt + n, N - 1);
-#pragma unroll
-                for (int s = 0; s < DS; ++s) kr[slot][kt * DS + s] = load16(kbase + (size_t)key * D + 32 * s + 8 * g);
+            for (int f = 0; f < FR; ++f) {
+                const int p = 64 * f + lane;
+                const int row = p / CPR, cc = (p % CPR) ^ (row & (CPR - 1));
+                const int key = min(key0 + row, N - 1);
+                global_to_lds16(kbase + (size_t)key * D + cc * 8, lds_addr(slot + 1024 * f));
             }
         };
-#pragma unroll
-        for (int u = 0; u < (KR < UW ? KR : UW); ++u) load_k(u, u);
+        issue_k(0);
+        if (UW > 1) issue_k(1);
 
         f32x4 t[UW][2][NT];
 #pragma unroll
         for (int u = 0; u < UW; ++u) {
-            const int slot = u % KR;
+            // K(u) is complete once at most the next unit's copies are outstanding
+            if (u + 1 < UW) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(FR) : "memory");
+            else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            const char* kslot = slot_of(u);
+            u32x4 kf[2][DS];
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int s = 0; s < DS; ++s) {
+                    const int r = 16 * kt + n, c = 4 * s + g;
+                    kf[kt][s] = *(const u32x4*)(kslot + r * (2 * D) + ((c ^ (r & (CPR - 1))) << 4));
+                }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this slot has been read
+            if (u + 2 < UW) issue_k(u + 2);
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
                 float pm = kNegInf;
@@ -131,7 +151,7 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
                 for (int kt = 0; kt < 2; ++kt) {
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int s = 0; s < DS; ++s) acc = mfma16x16x32(as_bf16x8(kr[slot][kt * DS + s]), qf[nt][s], acc);
+                    for (int s = 0; s < DS; ++s) acc = mfma16x16x32(as_bf16x8(kf[kt][s]), qf[nt][s], acc);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int key = ukey0[u] + 16 * kt + 4 * g + i;
@@ -146,7 +166,6 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
                 pm = fmaxf(pm, wave_shfl_xor(pm, 32));
                 if (uok[u] && g == 0) lds_pmax[parity][(wave + W * u) * HT + nt * 16 + n] = pm;
             }
-            if (u + KR < UW) load_k(slot, u + KR);
         }
         __syncthreads();
 
