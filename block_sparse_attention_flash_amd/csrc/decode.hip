@@ -39,7 +39,16 @@ namespace blasst {
 
 namespace {
 
-template <int D, int BC, int NT, int UW, int W, int KR>
+// s_waitcnt vmcnt(F * n) for a wave-uniform n in 0..3 (the count is an immediate)
+template <int F>
+__device__ __forceinline__ void wait_vm(int n) {
+    if (n <= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if (n == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(F) : "memory");
+    else if (n == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * F) : "memory");
+    else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * F) : "memory");
+}
+
+template <int D, int BC, int NT, int UW, int W, int NSLOT>
 __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
     constexpr int KG = BC / 32;           // 32-key units per block
     constexpr int UPP = W * UW;           // units per phase
@@ -52,9 +61,10 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
     constexpr int VSLOT = 32 * D * 2;     // bytes of one 32-row V slice
     static_assert(UPP % KG == 0, "units must tile the phase");
     static_assert(BPP <= 32, "decision masks are 32-bit");
-    static_assert(W * DT * 4 * 64 * 4 <= 2 * W * VSLOT, "O reduction must fit the V staging area");
+    static_assert(W * DT * 4 * 64 * 4 <= NSLOT * W * VSLOT, "O reduction must fit the staging area");
+    static_assert(NSLOT >= 2 && NSLOT <= 4, "staging ring depth");
 
-    __shared__ __attribute__((aligned(16))) char lds_v[2 * W * VSLOT];
+    __shared__ __attribute__((aligned(16))) char lds_v[NSLOT * W * VSLOT];
     __shared__ float lds_pmax[2][UPP * HT];
     __shared__ float lds_l[W][64];
 
@@ -111,7 +121,8 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
         // two staging slots -- the same slots and copy pattern as the V pass --
         // and are read back in the MFMA A layout (ds_read_b128).  Units past
         // the split re-read its last block (cached), so the wait counts are fixed.
-        auto slot_of = [&](int u) { return lds_v + (2 * wave + (u & 1)) * VSLOT; };
+        // Unit u of the wave uses slot u % NSLOT.
+        auto slot_of = [&](int u) { return lds_v + (NSLOT * wave + (u % NSLOT)) * VSLOT; };
         auto issue_k = [&](int u) {
             const int U = wave + W * u;
             const int key0 = min(p0 + U / KG, j1 - 1) * BC + (U % KG) * 32;
@@ -124,15 +135,15 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
                 global_to_lds16(kbase + (size_t)key * D + cc * 8, lds_addr(slot + 1024 * f));
             }
         };
-        issue_k(0);
-        if (UW > 1) issue_k(1);
+#pragma unroll
+        for (int u = 0; u < (NSLOT < UW ? NSLOT : UW); ++u) issue_k(u);
 
         f32x4 t[UW][2][NT];
 #pragma unroll
         for (int u = 0; u < UW; ++u) {
-            // K(u) is complete once at most the next unit's copies are outstanding
-            if (u + 1 < UW) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(FR) : "memory");
-            else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            // K(u) is complete once only the copies of the units issued after it
+            // (u + 1 .. u + NSLOT - 1) are outstanding
+            wait_vm<FR>(min(NSLOT - 1, UW - 1 - u));
             const char* kslot = slot_of(u);
             u32x4 kf[2][DS];
 #pragma unroll
@@ -143,7 +154,7 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
                     kf[kt][s] = *(const u32x4*)(kslot + r * (2 * D) + ((c ^ (r & (CPR - 1))) << 4));
                 }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this slot has been read
-            if (u + 2 < UW) issue_k(u + 2);
+            if (u + NSLOT < UW) issue_k(u + NSLOT);
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
                 float pm = kNegInf;
@@ -218,8 +229,12 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
         for (int u = 0; u < UW; ++u) kept[u] = uok[u] && ((vkeep >> ((wave + W * u) / KG)) & 1u);
 
+        uint32_t km = 0;  // kept units of this wave (the same in every lane)
+#pragma unroll
+        for (int u = 0; u < UW; ++u) km |= (uint32_t)kept[u] << u;
+        km = (uint32_t)__builtin_amdgcn_readfirstlane((int)km);
         auto issue_v = [&](int u) {
-            const char* slot = lds_v + (2 * wave + (u & 1)) * VSLOT;
+            const char* slot = slot_of(u);
 #pragma unroll
             for (int f = 0; f < FR; ++f) {
                 const int p = 64 * f + lane;
@@ -228,8 +243,9 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
                 global_to_lds16(vbase + (size_t)key * D + cc * 8, lds_addr(slot + 1024 * f));
             }
         };
-        if (kept[0]) issue_v(0);
-        if (UW > 1 && kept[UW > 1 ? 1 : 0]) issue_v(1);
+#pragma unroll
+        for (int u = 0; u < (NSLOT < UW ? NSLOT : UW); ++u)
+            if ((km >> u) & 1u) issue_v(u);
 
         // rescale the running state to the phase's new max (overlaps the V loads)
 #pragma unroll
@@ -241,11 +257,11 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
 
 #pragma unroll
         for (int u = 0; u < UW; ++u) {
-            if (kept[u]) {
-                // V(u) is complete once at most the next unit's loads are outstanding
-                if (u + 1 < UW && kept[u + 1 < UW ? u + 1 : u]) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(FR) : "memory");
-                else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                const lds_char* vslot = (const lds_char*)(lds_v + (2 * wave + (u & 1)) * VSLOT);
+            if ((km >> u) & 1u) {
+                // V(u) is complete once only the kept units issued after it
+                // (among u + 1 .. u + NSLOT - 1) are outstanding
+                wait_vm<FR>(__builtin_popcount((km >> (u + 1)) & ((1u << (NSLOT - 1)) - 1u)));
+                const lds_char* vslot = (const lds_char*)slot_of(u);
                 const int blk_bit = (wave + W * u) / KG;
                 bf16x8 pf[NT];
 #pragma unroll
@@ -275,9 +291,9 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
                     for (int nt = 0; nt < NT; ++nt) oacc[nt][dt] = mfma16x16x32(av, pf[nt], oacc[nt][dt]);
                 }
             }
-            if (u + 2 < UW && kept[u + 2 < UW ? u + 2 : u]) {
-                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // slot (u & 1) has been read
-                issue_v(u + 2);
+            if (u + NSLOT < UW && ((km >> (u + NSLOT < UW ? u + NSLOT : 0)) & 1u)) {
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // slot u % NSLOT has been read
+                issue_v(u + NSLOT);
             }
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -363,16 +379,22 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restri
     if (e == 0 && lse != nullptr) lse[row] = total;
 }
 
-template <int D, int BC, int NT, int UW, int W, int KR>
+template <int D, int BC, int NT, int UW, int W, int NSLOT>
 hipError_t launch_split(const DecodeArgs& a, hipStream_t stream) {
     dim3 grid(a.S, a.Hkv, a.B);
-    hipLaunchKernelGGL((decode_split_kernel<D, BC, NT, UW, W, KR>), grid, dim3(64 * W), 0, stream, a);
+    hipLaunchKernelGGL((decode_split_kernel<D, BC, NT, UW, W, NSLOT>), grid, dim3(64 * W), 0, stream, a);
     return hipGetLastError();
 }
 
 template <int D, int BC>
 hipError_t launch_split_nt(const DecodeArgs& a, hipStream_t stream) {
-    if (a.G <= 16) return launch_split<D, BC, 1, 8, 8, 2>(a, stream);
+    // Up to 16 heads: 128 KiB of copies in flight per workgroup either way.  With
+    // few workgroups (one per CU) eight waves x two slots measured faster; with
+    // many, one wave per SIMD x four slots (the SIMD's second wave lags otherwise).
+    if (a.G <= 16) {
+        if ((int64_t)a.S * a.Hkv * a.B <= 256) return launch_split<D, BC, 1, 8, 8, 2>(a, stream);
+        return launch_split<D, BC, 1, 16, 4, 4>(a, stream);
+    }
     if (a.G <= 32) return launch_split<D, BC, 2, 4, 8, 2>(a, stream);
     return launch_split<D, BC, 4, 2, 4, 2>(a, stream);
 }
