@@ -34,6 +34,41 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 METRIC = "decode µs & HBM GB/s at 32K; prefill TFLOP/s at 32K; block sparsity %"
 
 
+# Counter-measured HBM bytes per launch live in the committed profile records
+# (profiles/*.md, a "key: value" block).  A record counts only while the
+# kernel's sources hash to the value it was taken with.
+KERNEL_SOURCES = {
+    "decode_split_kernel": ["decode.hip", "device_common.h", "kernels.h"],
+    "prefill_kernel": ["prefill.hip", "device_common.h", "kernels.h"],
+}
+
+
+def source_hash(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "block_sparse_attention_flash_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from FETCH_SIZE / WRITE_SIZE (copy-calibrated), or None if stale or absent."""
+    import glob
+    want = source_hash(kernel)
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        rec = {}
+        with open(path, encoding="utf-8") as fh:
+            for line in fh:
+                line = line.strip()
+                if ":" in line and " " not in line.split(":", 1)[0]:
+                    k, v = line.split(":", 1)
+                    rec[k] = v.strip()
+        if rec.get("kernel") == kernel and rec.get("workload") == workload and "traffic_bytes_per_launch" in rec:
+            return int(rec["traffic_bytes_per_launch"]) if rec.get("source_sha256_16") == want else None
+    return None
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -239,7 +274,8 @@ def bench_prefill(args, lib, torch, W):
     dense = out["0"]["ms"]
     for k, v in out.items():
         v["speedup_vs_lambda0"] = round(dense / v["ms"], 4)
-    return dict(workload=w.name, B=B, Hq=Hq, Hkv=w.Hkv, d=d, T=T, Bc=Bc, by_lambda=out)
+    return dict(workload=w.name, B=B, Hq=Hq, Hkv=w.Hkv, d=d, T=T, Bc=Bc, by_lambda=out,
+                hbm_traffic_bytes_per_launch=measured_traffic("prefill_kernel", w.name))
 
 
 def cpu_baseline(args, dres):
@@ -305,7 +341,8 @@ def main():
                    "Hkv": w.Hkv, "d": w.d, "context": w.T, "Bc": w.Bc, "lambda": w.lambdas[0],
                    "num_splits": w.num_splits, "kv_copies_rotated": args.copies},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("decode_split_kernel", w.name),
                      "kernel": "decode_split_kernel", "bytes_per_launch": by["split"],
                      "avg_launch_us": round(d["split_ms"] * 1e3, 3)},
         "decode": {"step_us": round(d["step_ms"] * 1e3, 3), "split_kernel_us": round(d["split_ms"] * 1e3, 3),
