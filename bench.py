@@ -86,6 +86,7 @@ def parse():
 
 
 COPY_BYTES = 512 << 20  # plain device-to-device copy used to calibrate byte counters
+TRIALS = 7  # repeated kernel-only timing trials (median reported)
 
 
 def profile_target(args, lib, torch, W):
@@ -206,14 +207,18 @@ def bench_decode(args, lib, torch, W):
     wall = time.perf_counter() - t0
     step_ms = start.elapsed_time(stop) / args.steps
 
-    # the split kernel alone: K back-to-back launches between one pair of events
-    torch.cuda.synchronize()
-    start.record(stream)
-    for s in range(args.steps):
-        check(decode_fn(*sargs[s % len(sargs)]))
-    stop.record(stream)
-    torch.cuda.synchronize()
-    split_ms = start.elapsed_time(stop) / args.steps
+    # the split kernel alone: TRIALS trials of K back-to-back launches, each
+    # between one pair of events on the launch stream; the median trial is used
+    trials = []
+    for _ in range(TRIALS):
+        torch.cuda.synchronize()
+        start.record(stream)
+        for s in range(args.steps):
+            check(decode_fn(*sargs[s % len(sargs)]))
+        stop.record(stream)
+        torch.cuda.synchronize()
+        trials.append(start.elapsed_time(stop) / args.steps)
+    split_ms = float(np.median(trials))
 
     # dense-equivalent reference (lambda = 0): same kernels, nothing skipped
     for s in range(args.warmup):
@@ -232,8 +237,8 @@ def bench_decode(args, lib, torch, W):
     torch.cuda.synchronize()
     sk, vsk = skip.cpu().numpy(), vskip.cpu().numpy()
     by = decode_bytes(w, vsk)
-    return dict(w=w, x=x, step_ms=step_ms, split_ms=split_ms, dense_step_ms=dense_step_ms, wall=wall,
-                bytes=by, block_sparsity=float(sk.mean()), vload_sparsity=float(vsk.mean()))
+    return dict(w=w, x=x, step_ms=step_ms, split_ms=split_ms, split_trials_ms=trials, dense_step_ms=dense_step_ms,
+                wall=wall, bytes=by, block_sparsity=float(sk.mean()), vload_sparsity=float(vsk.mean()))
 
 
 def bench_prefill(args, lib, torch, W):
@@ -278,6 +283,17 @@ def bench_prefill(args, lib, torch, W):
                 hbm_traffic_bytes_per_launch=measured_traffic("prefill_kernel", w.name))
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(args, dres):
     import oracle
     w = dres["w"]
@@ -295,9 +311,21 @@ def cpu_baseline(args, dres):
     per = el / n
     by = decode_bytes(w, r["vskip_full"])
     gbs = (by["split"] + by["combine"]) / per / 1e9
+    # one thread: one decode_32k step, and the 1K prefill (all heads)
+    t1 = time.perf_counter()
+    oracle.decode(x["q"], x["k"], x["v"], w.Bc, w.lambdas[0], w.num_splits, threads=1)
+    one_decode = time.perf_counter() - t1
+    import workloads as W
+    wp = W.CONFIGS["prefill_1k_tiny"]
+    xp = W.generate(wp)
+    t1 = time.perf_counter()
+    oracle.prefill(xp["q"], xp["k"], xp["v"], wp.Bc, wp.lambdas[0], threads=1)
+    one_prefill = time.perf_counter() - t1
     return dict(value=round(gbs, 4), unit="GB/s", cores=threads, kind="oracle",
                 sample="full decode_32k step (all 32 heads, 16 splits) + combine, repeated %d times in %.1f s; "
-                       "%.1f ms per step" % (n, el, per * 1e3))
+                       "%.1f ms per step" % (n, el, per * 1e3),
+                cpu_model=cpu_model(),
+                single_thread_s={"decode_32k_step": round(one_decode, 3), "prefill_1k_tiny": round(one_prefill, 3)})
 
 
 def main():
@@ -346,6 +374,10 @@ def main():
                      "kernel": "decode_split_kernel", "bytes_per_launch": by["split"],
                      "avg_launch_us": round(d["split_ms"] * 1e3, 3)},
         "decode": {"step_us": round(d["step_ms"] * 1e3, 3), "split_kernel_us": round(d["split_ms"] * 1e3, 3),
+                   "split_kernel_trials_us": {"n": len(d["split_trials_ms"]),
+                                              "min": round(min(d["split_trials_ms"]) * 1e3, 3),
+                                              "median": round(d["split_ms"] * 1e3, 3),
+                                              "max": round(max(d["split_trials_ms"]) * 1e3, 3)},
                    "dense_step_us": round(d["dense_step_ms"] * 1e3, 3),
                    "speedup_vs_lambda0": round(d["dense_step_ms"] / d["step_ms"], 4),
                    "block_sparsity": round(d["block_sparsity"], 5), "vload_sparsity": round(d["vload_sparsity"], 5),
