@@ -82,6 +82,8 @@ def parse():
     p.add_argument("--profile-target", choices=["decode", "prefill", "copy"], default=None,
                    help="run only one kernel a few times (for hardware-counter collection) and exit")
     p.add_argument("--profile-launches", type=int, default=10)
+    p.add_argument("--length-sweep", action="store_true",
+                   help="instead of the bench: sparsity drift over 4K-128K context and the lambda = a/L calibration")
     return p.parse_args()
 
 
@@ -135,6 +137,56 @@ def profile_target(args, lib, torch, W):
                                   ctypes.c_double(1e-3), 1, sp) == 0
     torch.cuda.synchronize()
     print("prefill_32k: %d launches at lambda=1e-3" % n)
+
+
+SWEEP_LAMBDAS = tuple(float(x) for x in np.geomspace(1e-5, 0.9, 50))  # candidate thresholds
+SWEEP_FIXED = (1e-3, 3e-3)
+SWEEP_TARGETS = (0.5, 0.7)
+
+
+def sweep_margins(kind, L, split, W, bsa, B=None):
+    """GPU decision margins of one length-sweep batch (flattened) and the margin kernel's time."""
+    import torch
+    w = W.sweep_workload(kind, L, split, B)
+    x = W.generate(w, parts=("q", "k"))
+    q, k = dev(x["q"]), dev(x["k"])
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    if kind == "decode":
+        m, _ = bsa.decode_margins(q, k, w.num_splits, Bc=w.Bc)
+    else:
+        m = bsa.prefill_margins(q, k, Bc=w.Bc, causal=True)
+    e1.record()
+    torch.cuda.synchronize()
+    return m.cpu().numpy().ravel(), e0.elapsed_time(e1)
+
+
+def length_sweep(kind, lengths, calib_lengths, W, bsa, B=None, log=None):
+    """Sparsity at fixed lambda over context lengths (the drift), then the one-pass calibration of
+    lambda = alpha * exp(beta * S) / L on the calibration sequences and its sparsity on other sequences."""
+    from block_sparse_attention_flash_amd import policy
+    cal, ev, ms = {}, {}, {}
+    for L in lengths:
+        if L in calib_lengths:
+            cal[L], _ = sweep_margins(kind, L, "calibration", W, bsa, B)
+        ev[L], ms[L] = sweep_margins(kind, L, "evaluation", W, bsa, B)
+        if log:
+            log("%s L=%d: %d decisions, margin kernel %.3f ms" % (kind, L, np.count_nonzero(~np.isnan(ev[L])), ms[L]))
+    a, s = policy.calibration_points([cal[L] for L in calib_lengths], list(calib_lengths), SWEEP_LAMBDAS)
+    alpha, beta = policy.fit_exponential(a, s)
+    out = {"lengths": list(lengths), "calibration_lengths": list(calib_lengths),
+           "margin_kernel_ms": [round(ms[L], 3) for L in lengths],
+           "fixed_lambda": {str(lam): [round(float(policy.sparsity_at(ev[L], [lam])[0]), 4) for L in lengths]
+                            for lam in SWEEP_FIXED},
+           "fit": {"alpha": alpha, "beta": beta, "points": int(len(a))}, "calibrated": {}}
+    for S in SWEEP_TARGETS:
+        lams = [policy.lambda_for(S, L, alpha, beta) for L in lengths]
+        sp = [float(policy.sparsity_at(ev[L], [lam])[0]) for L, lam in zip(lengths, lams)]
+        out["calibrated"][str(S)] = {"a": alpha * float(np.exp(beta * S)), "lambda": lams,
+                                     "sparsity": [round(v, 4) for v in sp],
+                                     "mean_abs_dev": round(float(np.mean(np.abs(np.asarray(sp) - S))), 4),
+                                     "spread": round(max(sp) - min(sp), 4)}
+    return out
 
 
 def dev(bits):
@@ -341,6 +393,12 @@ def main():
     lib = bsa._load()
     if args.profile_target:
         profile_target(args, lib, torch, W)
+        return
+    if args.length_sweep:
+        say = lambda msg: print(msg, file=sys.stderr, flush=True)  # noqa: E731
+        rep = {"decode": length_sweep("decode", W.SWEEP_LENGTHS, W.SWEEP_LENGTHS[:5], W, bsa, log=say),
+               "prefill": length_sweep("prefill", W.SWEEP_LENGTHS, W.SWEEP_LENGTHS[:5], W, bsa, log=say)}
+        print(json.dumps({"length_sweep": rep}), flush=True)
         return
 
     d = bench_decode(args, lib, torch, W)

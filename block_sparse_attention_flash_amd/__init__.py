@@ -7,8 +7,9 @@ every step of the computation runs in the library's HIP kernels.  If the
 library is missing or fails to load, importing the binding's functions raises:
 there is no CPU or PyTorch fallback.
 
-The convenience wrappers ``prefill``, ``decode`` and ``decode_combine``
-allocate their outputs with PyTorch and call the entry points.
+The convenience wrappers ``prefill``, ``decode``, ``decode_combine``,
+``prefill_margins`` and ``decode_margins`` allocate their outputs with PyTorch
+and call the entry points.
 """
 from __future__ import annotations
 
@@ -18,8 +19,9 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["blasst_prefill", "blasst_decode", "blasst_decode_combine", "status_string",
-           "prefill", "decode", "decode_combine", "BlasstError", "library_path", "build"]
+__all__ = ["blasst_prefill", "blasst_decode", "blasst_decode_combine", "blasst_prefill_margins",
+           "blasst_decode_margins", "status_string", "prefill", "decode", "decode_combine", "prefill_margins",
+           "decode_margins", "BlasstError", "library_path", "build"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libblasst.so")
@@ -58,6 +60,10 @@ def _load():
         lib.blasst_decode.restype = i
         lib.blasst_decode_combine.argtypes = [P, P, P, P, i, i, i, i, P]
         lib.blasst_decode_combine.restype = i
+        lib.blasst_prefill_margins.argtypes = [P, P, P, i, i, i, i, i, i, i, P]
+        lib.blasst_prefill_margins.restype = i
+        lib.blasst_decode_margins.argtypes = [P, P, P, P, i, i, i, i, i, i, i, P]
+        lib.blasst_decode_margins.restype = i
         lib.blasst_status_string.argtypes = [i]
         lib.blasst_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -160,6 +166,66 @@ def blasst_decode_combine(o_part: torch.Tensor, lse_part: torch.Tensor, o: torch
     st = _load().blasst_decode_combine(_ptr(o_part), _ptr(lse_part), _ptr(o), _ptr(lse), B, Hq, d, S,
                                        _stream(stream))
     _check("blasst_decode_combine", st)
+
+
+def blasst_prefill_margins(q: torch.Tensor, k: torch.Tensor, margin: torch.Tensor, Bc: int,
+                           causal: bool = True, stream=None) -> None:
+    """q [B,Hq,T,d], k [B,Hkv,T,d] bf16 -> margin [B,Hq,nq,nq] fp32 (natural log; NaN = not visited)."""
+    _need(q, "q", torch.bfloat16)
+    _need(k, "k", torch.bfloat16)
+    _need(margin, "margin", torch.float32)
+    B, Hq, T, d = q.shape
+    Hkv = k.shape[1]
+    if Hkv == 0 or Hq % Hkv or k.shape != (B, Hkv, T, d):
+        raise ValueError("inconsistent prefill shapes")
+    nq = -(-T // Bc)
+    if margin.shape != (B, Hq, nq, nq):
+        raise ValueError("margin must be [B,Hq,nq,nq]")
+    st = _load().blasst_prefill_margins(_ptr(q), _ptr(k), _ptr(margin), B, Hq, T, d, Hq // Hkv, Bc,
+                                        int(bool(causal)), _stream(stream))
+    _check("blasst_prefill_margins", st)
+
+
+def blasst_decode_margins(q: torch.Tensor, k: torch.Tensor, margin: torch.Tensor, vmargin: Optional[torch.Tensor],
+                          Bc: int, num_splits: int, stream=None) -> None:
+    """q [B,Hq,1,d], k [B,Hkv,N,d] bf16 -> margin [B,Hq,nk], vmargin [B,Hkv,nk] or None (fp32, natural log)."""
+    _need(q, "q", torch.bfloat16)
+    _need(k, "k", torch.bfloat16)
+    _need(margin, "margin", torch.float32)
+    B, Hq, one, d = q.shape
+    Hkv, N = k.shape[1], k.shape[2]
+    if one != 1 or Hkv == 0 or Hq % Hkv or k.shape != (B, Hkv, N, d):
+        raise ValueError("inconsistent decode shapes")
+    nk = -(-N // Bc)
+    if margin.shape != (B, Hq, nk):
+        raise ValueError("margin must be [B,Hq,nk]")
+    if vmargin is not None:
+        _need(vmargin, "vmargin", torch.float32)
+        if vmargin.shape != (B, Hkv, nk):
+            raise ValueError("vmargin must be [B,Hkv,nk]")
+    st = _load().blasst_decode_margins(_ptr(q), _ptr(k), _ptr(margin), _ptr(vmargin), B, Hq, N, d, Hq // Hkv, Bc,
+                                       num_splits, _stream(stream))
+    _check("blasst_decode_margins", st)
+
+
+def prefill_margins(q, k, Bc: int = 128, causal: bool = True) -> torch.Tensor:
+    """Allocating wrapper: margin fp32 [B,Hq,nq,nq]."""
+    B, Hq, T, d = q.shape
+    nq = -(-T // Bc)
+    margin = torch.empty((B, Hq, nq, nq), dtype=torch.float32, device=q.device)
+    blasst_prefill_margins(q, k, margin, Bc, causal)
+    return margin
+
+
+def decode_margins(q, k, num_splits: int, Bc: int = 128) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Allocating wrapper: (margin [B,Hq,nk], vmargin [B,Hkv,nk]), fp32."""
+    B, Hq, _, d = q.shape
+    Hkv, N = k.shape[1], k.shape[2]
+    nk = -(-N // Bc)
+    margin = torch.empty((B, Hq, nk), dtype=torch.float32, device=q.device)
+    vmargin = torch.empty((B, Hkv, nk), dtype=torch.float32, device=q.device)
+    blasst_decode_margins(q, k, margin, vmargin, Bc, num_splits)
+    return margin, vmargin
 
 
 def prefill(q, k, v, lam: float, Bc: int = 128, causal: bool = True,

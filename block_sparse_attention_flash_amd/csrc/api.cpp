@@ -123,6 +123,82 @@ BLASST_EXPORT blasst_status blasst_decode_combine(const float* o_part, const flo
     }
 }
 
+BLASST_EXPORT blasst_status blasst_prefill_margins(const void* q, const void* k, float* margin, int B, int Hq, int T,
+                                                   int d, int gqa_ratio, int Bc, int causal, blasst_stream_t stream) {
+    try {
+        if (B < 0 || Hq < 0 || T < 0 || d <= 0 || Bc <= 0 || gqa_ratio < 1) return BLASST_ERR_INVALID_ARG;
+        if (Hq % gqa_ratio != 0 || (causal != 0 && causal != 1)) return BLASST_ERR_INVALID_ARG;
+        if (!supported_dim(d) || !supported_dim(Bc)) return BLASST_ERR_UNSUPPORTED;
+        if ((int64_t)B * Hq * T == 0) return BLASST_OK;  // nothing to do; pointers are not read
+        if (!q || !k || !margin) return BLASST_ERR_INVALID_ARG;
+        if (!aligned16(q) || !aligned16(k)) return BLASST_ERR_INVALID_ARG;
+        const int64_t nq = (T + Bc - 1) / Bc;
+        if (nq * B * Hq > INT32_MAX) return BLASST_ERR_UNSUPPORTED;
+
+        blasst::PrefillArgs a;
+        a.q = static_cast<const uint16_t*>(q);
+        a.k = static_cast<const uint16_t*>(k);
+        a.v = nullptr;
+        a.o = nullptr;
+        a.lse = nullptr;
+        a.mask = nullptr;
+        a.margin = margin;
+        a.B = B;
+        a.Hq = Hq;
+        a.G = gqa_ratio;
+        a.Hkv = Hq / gqa_ratio;
+        a.T = T;
+        a.nq = (int)nq;
+        a.nk = (int)nq;
+        a.causal = causal;
+        a.score_scale = static_cast<float>(kLog2e / std::sqrt((double)d));
+        a.thr = -INFINITY;
+        return from_hip(blasst::launch_prefill_margins(a, d, Bc, reinterpret_cast<hipStream_t>(stream)));
+    } catch (...) {
+        return BLASST_ERR_INTERNAL;
+    }
+}
+
+BLASST_EXPORT blasst_status blasst_decode_margins(const void* q, const void* k, float* margin, float* vmargin, int B,
+                                                  int Hq, int N, int d, int gqa_ratio, int Bc, int num_splits,
+                                                  blasst_stream_t stream) {
+    try {
+        if (B < 0 || Hq < 0 || N <= 0 || d <= 0 || Bc <= 0 || gqa_ratio < 1) return BLASST_ERR_INVALID_ARG;
+        if (Hq % gqa_ratio != 0) return BLASST_ERR_INVALID_ARG;
+        const int64_t nk = ((int64_t)N + Bc - 1) / Bc;
+        if (num_splits < 1 || num_splits > nk) return BLASST_ERR_INVALID_ARG;
+        if (!supported_dim(d) || !supported_dim(Bc)) return BLASST_ERR_UNSUPPORTED;
+        if (gqa_ratio > 64) return BLASST_ERR_UNSUPPORTED;
+        if ((int64_t)B * Hq == 0) return BLASST_OK;  // nothing to do; pointers are not read
+        if (!q || !k || !margin) return BLASST_ERR_INVALID_ARG;
+        if (!aligned16(q) || !aligned16(k)) return BLASST_ERR_INVALID_ARG;
+        if (B > 65535 || Hq / gqa_ratio > 65535) return BLASST_ERR_UNSUPPORTED;
+
+        blasst::DecodeArgs a;
+        a.q = static_cast<const uint16_t*>(q);
+        a.k = static_cast<const uint16_t*>(k);
+        a.v = nullptr;
+        a.o_part = nullptr;
+        a.lse_part = nullptr;
+        a.skip = nullptr;
+        a.vskip = nullptr;
+        a.margin = margin;
+        a.vmargin = vmargin;
+        a.B = B;
+        a.Hq = Hq;
+        a.G = gqa_ratio;
+        a.Hkv = Hq / gqa_ratio;
+        a.N = N;
+        a.nk = (int)nk;
+        a.S = num_splits;
+        a.score_scale = static_cast<float>(kLog2e / std::sqrt((double)d));
+        a.thr = -INFINITY;
+        return from_hip(blasst::launch_decode_margins(a, d, Bc, reinterpret_cast<hipStream_t>(stream)));
+    } catch (...) {
+        return BLASST_ERR_INTERNAL;
+    }
+}
+
 BLASST_EXPORT const char* blasst_status_string(blasst_status status) {
     switch (status) {
         case BLASST_OK: return "ok";

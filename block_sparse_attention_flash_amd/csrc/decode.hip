@@ -48,7 +48,12 @@ __device__ __forceinline__ void wait_vm(int n) {
     else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * F) : "memory");
 }
 
-template <int D, int BC, int NT, int UW, int W, int NSLOT>
+// MARGINS: the margin pass (BLASST blog, section on the one-pass calibration):
+// the K pass and the decisions' prefix max only, writing for every (head,
+// block) D = (m~ - m_new) in natural-log units and for every block the max of D
+// over the group's heads (skipped / V not loaded at lambda iff below ln lambda);
+// no V pass, no partial outputs.
+template <int D, int BC, int NT, int UW, int W, int NSLOT, bool MARGINS = false>
 __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
     constexpr int KG = BC / 32;           // 32-key units per block
     constexpr int UPP = W * UW;           // units per phase
@@ -184,6 +189,9 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
         uint32_t keep[NT];
         uint32_t vkeep = 0;
         float alpha[NT];
+        float vmax_blk[MARGINS ? BPP : 1];
+#pragma unroll
+        for (int bi = 0; bi < (MARGINS ? BPP : 1); ++bi) vmax_blk[bi] = kNegInf;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             float m = m_run[nt];
@@ -196,6 +204,19 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
                     for (int kg = 0; kg < KG; ++kg) bm = fmaxf(bm, lds_pmax[parity][(bi * KG + kg) * HT + nt * 16 + n]);
                     m = fmaxf(m, bm);
                     kb |= (uint32_t)(!((bm - m) < a.thr)) << bi;
+                    if constexpr (MARGINS) {
+                        const float dm = head_ok[nt] ? (bm - m) * kLn2 : kNegInf;
+                        if (wave == 0 && g == 0 && head_ok[nt])
+                            a.margin[((size_t)b * a.Hq + (size_t)hkv * G + nt * 16 + n) * nk + p0 + bi] = dm;
+                        if (a.vmargin != nullptr) {
+                            float vm = dm;
+                            vm = fmaxf(vm, __shfl_xor(vm, 1, 64));
+                            vm = fmaxf(vm, __shfl_xor(vm, 2, 64));
+                            vm = fmaxf(vm, __shfl_xor(vm, 4, 64));
+                            vm = fmaxf(vm, __shfl_xor(vm, 8, 64));
+                            vmax_blk[bi] = fmaxf(vmax_blk[bi], vm);
+                        }
+                    }
                 }
             }
             kb = head_ok[nt] ? kb : 0u;
@@ -208,6 +229,14 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
         vkeep |= __shfl_xor(vkeep, 2, 64);
         vkeep |= __shfl_xor(vkeep, 4, 64);
         vkeep |= __shfl_xor(vkeep, 8, 64);
+        if constexpr (MARGINS) {
+            if (a.vmargin != nullptr && wave == 0 && lane == 0) {
+                float* vrow = a.vmargin + ((size_t)b * a.Hkv + hkv) * nk + p0;
+                for (int bi = 0; bi < nb; ++bi) vrow[bi] = vmax_blk[bi];
+            }
+            __syncthreads();  // lds_pmax[parity] is rewritten two phases on
+            continue;         // the margin pass stops here: no V pass
+        }
 
         // decision bytes: one lane per (head, block)
         if (a.skip != nullptr) {
@@ -299,6 +328,7 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
 
+    if constexpr (MARGINS) return;
     // ---- reduce the waves' partial O^T and l; write the split's result
     __syncthreads();
     float* red = (float*)lds_v;  // [W waves][DT][4][64]
@@ -379,11 +409,19 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restri
     if (e == 0 && lse != nullptr) lse[row] = total;
 }
 
-template <int D, int BC, int NT, int UW, int W, int NSLOT>
+template <int D, int BC, int NT, int UW, int W, int NSLOT, bool MARGINS = false>
 hipError_t launch_split(const DecodeArgs& a, hipStream_t stream) {
     dim3 grid(a.S, a.Hkv, a.B);
-    hipLaunchKernelGGL((decode_split_kernel<D, BC, NT, UW, W, NSLOT>), grid, dim3(64 * W), 0, stream, a);
+    hipLaunchKernelGGL((decode_split_kernel<D, BC, NT, UW, W, NSLOT, MARGINS>), grid, dim3(64 * W), 0, stream, a);
     return hipGetLastError();
+}
+
+// The margin pass reads K only; the four-wave shape keeps 128 KiB in flight.
+template <int D, int BC>
+hipError_t launch_margins_nt(const DecodeArgs& a, hipStream_t stream) {
+    if (a.G <= 16) return launch_split<D, BC, 1, 16, 4, 4, true>(a, stream);
+    if (a.G <= 32) return launch_split<D, BC, 2, 4, 8, 2, true>(a, stream);
+    return launch_split<D, BC, 4, 2, 4, 2, true>(a, stream);
 }
 
 template <int D, int BC>
@@ -404,6 +442,11 @@ hipError_t launch_split_nt(const DecodeArgs& a, hipStream_t stream) {
 hipError_t launch_decode(const DecodeArgs& a, int d, int Bc, hipStream_t stream) {
     if (d == 128) return Bc == 128 ? launch_split_nt<128, 128>(a, stream) : launch_split_nt<128, 64>(a, stream);
     return Bc == 128 ? launch_split_nt<64, 128>(a, stream) : launch_split_nt<64, 64>(a, stream);
+}
+
+hipError_t launch_decode_margins(const DecodeArgs& a, int d, int Bc, hipStream_t stream) {
+    if (d == 128) return Bc == 128 ? launch_margins_nt<128, 128>(a, stream) : launch_margins_nt<128, 64>(a, stream);
+    return Bc == 128 ? launch_margins_nt<64, 128>(a, stream) : launch_margins_nt<64, 64>(a, stream);
 }
 
 hipError_t launch_decode_combine(const float* o_part, const float* lse_part, float* o, float* lse, int rows,

@@ -18,6 +18,8 @@ struct DecodeArgs {
     int B, Hq, Hkv, G, N, nk, S;
     float score_scale;  // log2(e) / sqrt(d): scores are handled in log2 units
     float thr;          // ln(lambda) * log2(e); -inf when lambda == 0
+    float* margin = nullptr;   // margin pass only: [B, Hq, nk]
+    float* vmargin = nullptr;  // margin pass only: [B, Hkv, nk] or null
 };
 
 // Causal / full prefill launch.
@@ -31,11 +33,14 @@ struct PrefillArgs {
     int B, Hq, Hkv, G, T, nq, nk, causal;
     float score_scale;
     float thr;
+    float* margin = nullptr;  // margin pass only: [B, Hq, nq, nk]
 };
 
 hipError_t launch_decode(const DecodeArgs& a, int d, int Bc, hipStream_t stream);
 hipError_t launch_decode_combine(const float* o_part, const float* lse_part, float* o, float* lse, int rows,
                                  int d, int S, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, int d, int Bc, hipStream_t stream);
+hipError_t launch_prefill_margins(const PrefillArgs& a, int d, int Bc, hipStream_t stream);
+hipError_t launch_decode_margins(const DecodeArgs& a, int d, int Bc, hipStream_t stream);
 
 }  // namespace blasst

@@ -368,3 +368,152 @@ hipError_t launch_prefill(const PrefillArgs& a, int d, int Bc, hipStream_t strea
 }
 
 }  // namespace blasst
+
+// ---------------------------------------------------------------------------
+// Decision margins of causal / full prefill, for every lambda at once.
+//
+// BLASST blog, section on the decision rule (Eq. 5) and section on the
+// one-pass calibration (Algorithm 2): the test of tile (i, j) for query row r
+// compares m~_r - m_r (block max minus the updated running max) with ln(lambda),
+// and the tile is skipped iff every row of the query block votes to skip.  A
+// skipped tile never moves the running max, so m_r is the prefix max of the
+// block maxima whatever lambda is; the tile's margin
+//     M(i, j) = max over the rows r of the query block of (m~_r - m_r) / sqrt(d)
+// (natural-log units) decides it for every lambda: skipped iff M < ln(lambda).
+// This pass forms S = Q K^T only (no softmax, no V) and writes M for visited
+// tiles, NaN for tiles above the diagonal.
+namespace blasst {
+namespace {
+
+template <int D, int BC>
+__global__ __launch_bounds__(2 * BC) void prefill_margin_kernel(PrefillArgs a) {
+    constexpr int NW = BC / 32;            // waves, 32 query rows each
+    constexpr int KT = BC / 32;
+    constexpr int DS = D / 16;
+    constexpr int CPR = D / 8;
+    constexpr int ROWB = 2 * D;
+    constexpr int TILE = BC * ROWB;
+    constexpr int CPW = TILE / (1024 * NW);
+    static_assert(TILE % (1024 * NW) == 0, "tile copies must split evenly over the waves");
+
+    __shared__ __attribute__((aligned(16))) char lds_k[2][TILE];
+    __shared__ float lds_m[2][NW];
+
+    const int bh_count = a.B * a.Hq;
+    const int L = blockIdx.x;
+    const int i = a.nq - 1 - L / bh_count;
+    const int bh = L % bh_count;
+    const int hq = bh % a.Hq, b = bh / a.Hq;
+    const int hkv = hq / a.G;
+    const int T = a.T;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 31, half = lane >> 5;
+    const int qidx = i * BC + 32 * wave + col;
+    const bool row_ok = qidx < T;
+    const float inv_sqrt_d = a.score_scale * 0.69314718055994531f;  // (log2 e / sqrt d) * ln 2
+
+    const uint16_t* kbase = a.k + ((size_t)b * a.Hkv + hkv) * (size_t)T * D;
+    bf16x8 qf[DS];
+    {
+        const uint16_t* qrow = a.q + (((size_t)b * a.Hq + hq) * T + min(qidx, T - 1)) * D;
+#pragma unroll
+        for (int s = 0; s < DS; ++s) qf[s] = as_bf16x8(load16(qrow + 16 * s + 8 * half));
+    }
+    const int last_row = min(T, (i + 1) * BC) - 1;
+    const int jend = a.causal ? last_row / BC + 1 : a.nk;
+
+    uint32_t toff[CPW];
+#pragma unroll
+    for (int f = 0; f < CPW; ++f) {
+        const int pp = (wave * CPW + f) * 64 + lane;
+        toff[f] = (uint32_t)((pp / CPR) * ROWB + (((pp % CPR) ^ chunk_swizzle<CPR>(pp / CPR)) << 4));
+    }
+    auto issue_k = [&](int j) {
+        const uint16_t* tbase = kbase + (size_t)j * BC * D;
+        const bool ragged = (j + 1) * BC > T;
+#pragma unroll
+        for (int f = 0; f < CPW; ++f) {
+            uint32_t off = toff[f];
+            if (ragged) off -= (uint32_t)(max(j * BC + (int)(off / ROWB) - (T - 1), 0) * ROWB);
+            global_to_lds16_sbase(tbase, off, lds_addr(&lds_k[j & 1][(wave * CPW + f) * 1024]));
+        }
+    };
+    const int kofs = col * ROWB + ((half ^ chunk_swizzle<CPR>(col)) << 4);
+
+    float* mrow = a.margin + (((size_t)b * a.Hq + hq) * a.nq + i) * a.nk;
+    float m = kNegInf;  // running (prefix) max of this lane's row, raw score units
+    issue_k(0);
+    for (int j = 0; j < jend; ++j) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's pieces of K(j)
+        __syncthreads();                                   // all of K(j); stage (j+1)&1 and lds_m[(j+1)&1] free
+        if (j + 1 < jend) issue_k(j + 1);
+        // the previous tile's margin: every wave's vote has landed
+        if (j > 0 && tid == 0) {
+            float x = kNegInf;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) x = fmaxf(x, lds_m[(j - 1) & 1][w]);
+            mrow[j - 1] = x;
+        }
+        f32x16 sacc[KT];
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+            sacc[kt] = f32x16{};
+#pragma unroll
+            for (int s = 0; s < DS; ++s) {
+                const u32x4 kf = *(const u32x4*)(&lds_k[j & 1][0] + 32 * kt * ROWB + (kofs ^ (32 * s)));
+                sacc[kt] = mfma32x32x16(as_bf16x8(kf), qf[s], sacc[kt]);
+            }
+        }
+        if ((a.causal && j == i) || (j + 1) * BC > T) {
+            const int lim = min(T - 1, a.causal ? qidx : T - 1) - j * BC - 4 * half;
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int o = 32 * kt + 8 * (e >> 2) + (e & 3);
+                    const uint32_t drop = (uint32_t)((lim - o) >> 31);
+                    const float sv = sacc[kt][e];  // scalar first (see the main kernel)
+                    sacc[kt][e] = __uint_as_float((__float_as_uint(sv) & ~drop) | (0xff800000u & drop));
+                }
+        }
+        float mt = kNegInf;
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) mt = fmaxf(mt, sacc[kt][e]);
+        mt = fmaxf(mt, wave_shfl_xor(mt, 32));
+        const float m_new = fmaxf(m, mt);
+        // a row that sees no key of the tile, or a row past T, votes skip with no effect
+        float dr = (row_ok && mt != kNegInf) ? (mt - m_new) * inv_sqrt_d : kNegInf;
+        m = m_new;
+#pragma unroll
+        for (int sh = 1; sh < 64; sh <<= 1) dr = fmaxf(dr, wave_shfl_xor(dr, sh));
+        if (lane == 0) lds_m[j & 1][wave] = dr;
+    }
+    __syncthreads();
+    if (tid == 0 && jend > 0) {
+        float x = kNegInf;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) x = fmaxf(x, lds_m[(jend - 1) & 1][w]);
+        mrow[jend - 1] = x;
+    }
+    for (int j = jend + tid; j < a.nk; j += blockDim.x) mrow[j] = __builtin_nanf("");
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+template <int D, int BC>
+hipError_t launch_margins(const PrefillArgs& a, hipStream_t stream) {
+    const dim3 grid((unsigned)a.nq * a.B * a.Hq);
+    hipLaunchKernelGGL((prefill_margin_kernel<D, BC>), grid, dim3(2 * BC), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill_margins(const PrefillArgs& a, int d, int Bc, hipStream_t stream) {
+    if (d == 128) return Bc == 128 ? launch_margins<128, 128>(a, stream) : launch_margins<128, 64>(a, stream);
+    return Bc == 128 ? launch_margins<64, 128>(a, stream) : launch_margins<64, 64>(a, stream);
+}
+
+}  // namespace blasst

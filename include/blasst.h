@@ -125,6 +125,40 @@ blasst_status blasst_decode_combine(const float* o_part, const float* lse_part, 
                                     float* lse, int B, int Hq, int d, int num_splits,
                                     blasst_stream_t stream);
 
+/*
+ * Decision margins for every lambda at once: the one-pass calibration tool
+ * (BLASST blog, section on the lambda = a/L policy and Algorithm 2, and section
+ * on the decision rule, Eq. 5).  A block's skip test compares D = m~ - m_new
+ * (block max minus the updated running max, scaled scores) with ln(lambda);
+ * since a skipped block never moves the running max, m_new is the prefix max
+ * of the block maxima and D does not depend on lambda.  So one pass gives the
+ * decision -- and the block sparsity -- at any lambda: skipped iff D < ln(lambda).
+ * These passes form S = Q K^T only: no softmax, no V, no outputs besides the
+ * margins.  Margins are fp32, natural-log units.
+ *
+ * blasst_prefill_margins: q, k as in blasst_prefill (v is not read).
+ *   margin  fp32 [B, Hq, ceil(T/Bc), ceil(T/Bc)]: for query block i and KV block
+ *           j, the max over the block's rows of D (the AND over rows becomes
+ *           a max: skipped iff every row's D < ln(lambda)); NaN for blocks the
+ *           causal mask leaves unvisited (j > i).
+ * Errors and argument rules as blasst_prefill (lambda absent); a null margin is
+ * INVALID_ARG.
+ */
+blasst_status blasst_prefill_margins(const void* q, const void* k, float* margin, int B, int Hq, int T, int d,
+                                     int gqa_ratio, int Bc, int causal, blasst_stream_t stream);
+
+/*
+ * blasst_decode_margins: q, k as in blasst_decode (v is not read).
+ *   margin   fp32 [B, Hq, ceil(N/Bc)]: D per query head and block, the running
+ *            max restarting at each of the num_splits splits.
+ *   vmargin  fp32 [B, Hkv, ceil(N/Bc)] or NULL: the max of D over the kv
+ *            group's heads (the V block is not loaded iff it is < ln(lambda)).
+ * Errors and argument rules as blasst_decode (lambda absent); a null margin is
+ * INVALID_ARG.
+ */
+blasst_status blasst_decode_margins(const void* q, const void* k, float* margin, float* vmargin, int B, int Hq,
+                                    int N, int d, int gqa_ratio, int Bc, int num_splits, blasst_stream_t stream);
+
 /* Static, human-readable name of a status code. */
 const char* blasst_status_string(blasst_status status);
 

@@ -27,7 +27,8 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert declared() == ["blasst_decode", "blasst_decode_combine", "blasst_prefill", "blasst_status_string"]
+    assert declared() == ["blasst_decode", "blasst_decode_combine", "blasst_decode_margins", "blasst_prefill",
+                          "blasst_prefill_margins", "blasst_status_string"]
 
 
 def test_exports_match_header(lib):
@@ -89,3 +90,31 @@ def test_combine_validation(lib):
     assert f(FAKE, FAKE, FAKE, None, 1, 4, 128, 0, None) == 1
     assert f(FAKE, FAKE, FAKE, None, 1, 4, 96, 2, None) == 2
     assert f(FAKE, FAKE, FAKE, None, 0, 4, 128, 2, None) == 0
+
+
+def prefill_margins(lib, q=FAKE, margin=FAKE, B=1, Hq=4, T=256, d=128, G=4, Bc=128, causal=1):
+    f = lib.blasst_prefill_margins
+    f.argtypes = [P, P, P, I, I, I, I, I, I, I, P]
+    return f(q, FAKE, margin, B, Hq, T, d, G, Bc, causal, None)
+
+
+def decode_margins(lib, q=FAKE, margin=FAKE, B=1, Hq=4, N=256, d=128, G=4, Bc=128, S=2):
+    f = lib.blasst_decode_margins
+    f.argtypes = [P, P, P, P, I, I, I, I, I, I, I, P]
+    return f(q, FAKE, margin, None, B, Hq, N, d, G, Bc, S, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(margin=None), 1), (dict(B=-1), 1), (dict(G=3), 1), (dict(causal=2), 1),
+    (dict(q=P(0x1008)), 1), (dict(d=96), 2), (dict(Bc=32), 2), (dict(B=0), 0), (dict(T=0), 0),
+])
+def test_prefill_margins_validation(lib, kw, status):
+    assert prefill_margins(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(margin=None), 1), (dict(N=0), 1), (dict(S=0), 1), (dict(S=3), 1), (dict(G=5), 1),
+    (dict(d=80), 2), (dict(Hq=128, G=128), 2), (dict(B=0), 0), (dict(Hq=0), 0),
+])
+def test_decode_margins_validation(lib, kw, status):
+    assert decode_margins(lib, **kw) == status

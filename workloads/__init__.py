@@ -19,6 +19,13 @@ the generator reproduces that shape with a planted direction:
   over an N(0, 1 + a^2/d) background.
 * optionally the last `window` keys get + c_w*u with c_w = window_logit*sqrt(d)/a,
   i.e. a recent-window bias of +window_logit in the scaled logit.
+* optionally (logit_tail = tau > 0) every key j gets + e_j*sqrt(d)/a * u with
+  e_j ~ Exponential(mean tau): an extra scaled logit of about e_j, so that the
+  scores have an exponential upper tail and the running max of a row grows like
+  tau * ln(position).  This is the length-sweep family: with sinks and hot keys
+  off, a fixed threshold skips more blocks the longer the context (the drift of
+  the blog's Table 6 / Fig 2 right), which the planted hot keys alone do not
+  show because their +8 logit fixes the max early.
 * every tensor is rounded to bfloat16 with round-to-nearest-even; the same
   bytes go to the GPU and to the oracle.
 
@@ -36,7 +43,7 @@ from typing import Optional, Sequence, Tuple, Union
 
 import numpy as np
 
-_TAG_DIR, _TAG_Q, _TAG_K, _TAG_V, _TAG_HOT, _TAG_RATE = 0, 1, 2, 3, 4, 5
+_TAG_DIR, _TAG_Q, _TAG_K, _TAG_V, _TAG_HOT, _TAG_RATE, _TAG_TAIL = 0, 1, 2, 3, 4, 5, 6
 
 
 @dataclasses.dataclass(frozen=True)
@@ -59,6 +66,7 @@ class Workload:
     window_logit: float = 3.0
     hot_logit: float = 8.0
     num_splits: int = 1  # decode only
+    logit_tail: float = 0.0  # mean of the exponential extra logit per key (0: off)
 
     @property
     def G(self) -> int:
@@ -101,6 +109,25 @@ CONFIGS = {
                                Bc=128, lambdas=(1e-3,), hot_rate=0.02, seed=_seed(5),
                                num_splits=8),
 }
+
+
+# The length-sweep family: heavy-tailed scores with no planted structure, at a
+# context length L per call.  "calibration" and "evaluation" draw different
+# sequences (seed sets), so a threshold fitted on one is checked on the other.
+SWEEP_LENGTHS = (4096, 8192, 16384, 32768, 65536, 131072)
+
+
+def sweep_workload(kind: str, L: int, split: str = "calibration", B: Optional[int] = None) -> Workload:
+    base = {"calibration": _seed(6), "evaluation": _seed(7)}[split]
+    if kind == "decode":
+        return Workload("sweep_decode_%d" % L, "decode", B=B or 4, Hq=32, Hkv=8, d=128, T=L, Bc=128,
+                        lambdas=(1e-3, 3e-3), hot_rate=0.0, seed=base + L // 1024, sinks=0,
+                        logit_tail=1.0, num_splits=1)
+    if kind == "prefill":
+        return Workload("sweep_prefill_%d" % L, "prefill", B=B or 1, Hq=32, Hkv=8, d=128, T=L, Bc=128,
+                        lambdas=(1e-3, 3e-3), hot_rate=0.0, seed=base + L // 1024 + 500, sinks=0,
+                        logit_tail=1.0)
+    raise ValueError("kind is prefill or decode")
 
 
 def _rng(w: Workload, tag: int, b: int = 0, h: int = 0) -> np.random.Generator:
@@ -157,6 +184,9 @@ def k_slice(w: Workload, b: int, hkv: int) -> np.ndarray:
     x[hot_positions(w, b, hkv)] += np.float32(w.amplitude) * u
     if w.window > 0:
         x[max(0, w.T - w.window):] += np.float32(w.window_coef) * u
+    if w.logit_tail > 0:
+        e = _rng(w, _TAG_TAIL, b, hkv).exponential(w.logit_tail, size=w.T).astype(np.float32)
+        x += (e * np.float32(math.sqrt(w.d) / w.amplitude))[:, None] * u[None, :]
     return to_bf16_bits(x)
 
 
