@@ -146,6 +146,60 @@ def decode(q, k, v, Bc: int, lam: float, num_splits: int,
     return out
 
 
+def prefill_ragged(q, k, v, lens, Bc: int, lam: float, causal: bool = True,
+                   threads: Optional[int] = None) -> dict:
+    """A ragged batch: sequence b is its first lens[b] rows of the padded [B,H,T,d]
+    tensors, and is exactly one plain prefill of that length (nothing else of the
+    batch is read).  Padded rows get o = 0 and lse = -inf; mask (and margin) entries
+    of query or KV blocks past a sequence's end are 2 (NaN), not visited.
+    Returns o_full, lse_full, mask_full, margin_full."""
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    B, Hq, T, d = q.shape
+    nq = -(-T // Bc)
+    o = np.zeros((B, Hq, T, d))
+    lse = np.full((B, Hq, T), -np.inf)
+    mask = np.full((B, Hq, nq, nq), 2, np.uint8)
+    margin = np.full((B, Hq, nq, nq), np.nan)
+    for b, L in enumerate(lens):
+        L = int(L)
+        if L <= 0:
+            continue
+        r = prefill(q[b:b + 1, :, :L], k[b:b + 1, :, :L], v[b:b + 1, :, :L], Bc, lam, causal=causal,
+                    threads=threads)
+        n = -(-L // Bc)
+        o[b, :, :L] = r["o_full"][0]
+        lse[b, :, :L] = r["lse_full"][0]
+        mask[b, :, :n, :n] = r["mask_full"][0]
+        margin[b, :, :n, :n] = r["margin_full"][0]
+    return dict(o_full=o, lse_full=lse, mask_full=mask, margin_full=margin)
+
+
+def decode_ragged(q, k, v, lens, Bc: int, lam: float, num_splits: int,
+                  threads: Optional[int] = None) -> dict:
+    """A ragged decode batch: sequence b attends to the first lens[b] keys of its
+    padded [N, d] cache rows, exactly one plain decode of that context length with
+    the same num_splits (a split left with no block holds o = 0, lse = -inf).  Mask
+    entries of blocks past a sequence's end are 2.  Returns o_part_full,
+    lse_part_full, skip_full, vskip_full."""
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    B, Hq, _, d = q.shape
+    Hkv, N = k.shape[1], k.shape[2]
+    nk, S = -(-N // Bc), num_splits
+    o_part = np.zeros((B, Hq, S, d))
+    lse_part = np.full((B, Hq, S), -np.inf)
+    skip = np.full((B, Hq, nk), 2, np.uint8)
+    vskip = np.full((B, Hkv, nk), 2, np.uint8)
+    for b, L in enumerate(lens):
+        L = max(int(L), 0)
+        r = decode(q[b:b + 1], k[b:b + 1, :, :L], v[b:b + 1, :, :L], Bc, lam, S, threads=threads)
+        n = -(-L // Bc)
+        o_part[b] = r["o_part_full"][0]
+        lse_part[b] = r["lse_part_full"][0]
+        skip[b, :, :n] = r["skip_full"][0]
+        vskip[b, :, :n] = r["vskip_full"][0]
+    return dict(o_part_full=o_part, lse_part_full=lse_part, skip_full=skip, vskip_full=vskip)
+
+
 def combine(o_part: np.ndarray, lse_part: np.ndarray):
     """Log-sum-exp merge over the split axis: o_part [..., S, d], lse_part [..., S]."""
     lead = o_part.shape[:-2]

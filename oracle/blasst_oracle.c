@@ -287,8 +287,10 @@ static void decode_unit(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                 widen(V + (size_t)c0 * d, vb, (size_t)nc * d);
                 accumulate_kept_block(&m, &l, acc, s, vb, nc, d, m_new);
             }
-            for (int e = 0; e < d; ++e) o_part[((size_t)g * S + sp) * d + e] = acc[e] / l;
-            lse_part[(size_t)g * S + sp] = m + log(l);
+            /* A split with no block (S > nk, or an empty context) contributes
+             * nothing to the merge: o = 0 and lse = -inf. */
+            for (int e = 0; e < d; ++e) o_part[((size_t)g * S + sp) * d + e] = (j1 > j0) ? acc[e] / l : 0.0;
+            lse_part[(size_t)g * S + sp] = (j1 > j0) ? m + log(l) : -INFINITY;
         }
     }
     for (int j = 0; j < nk; ++j) vmargin[j] = (thr == -INFINITY) ? INFINITY : best[j] - thr;
@@ -305,10 +307,10 @@ int oracle_decode(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                   double* o_part, double* lse_part, uint8_t* skip, uint8_t* vskip,
                   double* margin, double* vmargin, int nthreads)
 {
-    if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || N <= 0 || d <= 0 || Bc <= 0) return -1;
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || N < 0 || d <= 0 || Bc <= 0) return -1;
     if (!(lambda >= 0.0 && lambda < 1.0)) return -1;
     const int nk = ceil_div(N, Bc), G = Hq / Hkv, S = num_splits;
-    if (S < 1 || S > nk) return -1;
+    if (S < 1) return -1;
     const double thr = log_threshold(lambda);
 #ifdef _OPENMP
     if (nthreads > 0) omp_set_num_threads(nthreads);
@@ -337,6 +339,11 @@ int oracle_combine(const double* o_part, const double* lse_part, int rows, int S
         const double* ls = lse_part + (size_t)r * S;
         double top = -INFINITY;
         for (int s = 0; s < S; ++s) if (ls[s] > top) top = ls[s];
+        if (top == -INFINITY) {  /* every split empty: no key at all */
+            for (int e = 0; e < d; ++e) o[(size_t)r * d + e] = 0.0;
+            lse[r] = -INFINITY;
+            continue;
+        }
         double z = 0.0;
         for (int s = 0; s < S; ++s) z += exp(ls[s] - top);
         const double L = top + log(z);
