@@ -20,8 +20,9 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["blasst_prefill", "blasst_decode", "blasst_decode_combine", "blasst_prefill_margins",
-           "blasst_decode_margins", "status_string", "prefill", "decode", "decode_combine", "prefill_margins",
-           "decode_margins", "BlasstError", "library_path", "build"]
+           "blasst_decode_margins", "blasst_prefill_ragged", "blasst_decode_ragged", "status_string", "prefill",
+           "decode", "decode_combine", "prefill_margins", "decode_margins", "prefill_ragged", "decode_ragged",
+           "BlasstError", "library_path", "build"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libblasst.so")
@@ -64,6 +65,10 @@ def _load():
         lib.blasst_prefill_margins.restype = i
         lib.blasst_decode_margins.argtypes = [P, P, P, P, i, i, i, i, i, i, i, P]
         lib.blasst_decode_margins.restype = i
+        lib.blasst_prefill_ragged.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, i, d, i, P]
+        lib.blasst_prefill_ragged.restype = i
+        lib.blasst_decode_ragged.argtypes = [P, P, P, P, P, P, P, P, i, i, i, i, i, i, d, i, P]
+        lib.blasst_decode_ragged.restype = i
         lib.blasst_status_string.argtypes = [i]
         lib.blasst_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -93,11 +98,7 @@ def _need(t: torch.Tensor, name: str, dtype: torch.dtype):
         raise ValueError("%s must be a contiguous %s tensor on the GPU" % (name, dtype))
 
 
-def blasst_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
-                   lse: Optional[torch.Tensor], skip_mask: Optional[torch.Tensor], Bc: int,
-                   lam: float, causal: bool = True, stream=None) -> None:
-    """q [B,Hq,T,d], k/v [B,Hkv,T,d] bf16; o [B,Hq,T,d] fp32; lse [B,Hq,T] fp32 or None;
-    skip_mask [B,Hq,nq,nq] uint8 or None."""
+def _prefill_shapes(q, k, v, o, lse, skip_mask, Bc):
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, nm, torch.bfloat16)
     _need(o, "o", torch.float32)
@@ -114,16 +115,40 @@ def blasst_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.T
         _need(skip_mask, "skip_mask", torch.uint8)
         if skip_mask.shape != (B, Hq, nq, nq):
             raise ValueError("skip_mask must be [B,Hq,nq,nq]")
+    return B, Hq, T, d, Hkv
+
+
+def _lens(seq_lens, B):
+    _need(seq_lens, "seq_lens", torch.int32)
+    if seq_lens.shape != (B,):
+        raise ValueError("seq_lens must be [B]")
+    return seq_lens
+
+
+def blasst_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                   lse: Optional[torch.Tensor], skip_mask: Optional[torch.Tensor], Bc: int,
+                   lam: float, causal: bool = True, stream=None) -> None:
+    """q [B,Hq,T,d], k/v [B,Hkv,T,d] bf16; o [B,Hq,T,d] fp32; lse [B,Hq,T] fp32 or None;
+    skip_mask [B,Hq,nq,nq] uint8 or None."""
+    B, Hq, T, d, Hkv = _prefill_shapes(q, k, v, o, lse, skip_mask, Bc)
     st = _load().blasst_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(skip_mask), B, Hq, T, d,
                                 Hq // Hkv, Bc, float(lam), int(bool(causal)), _stream(stream))
     _check("blasst_prefill", st)
 
 
-def blasst_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o_part: torch.Tensor,
-                  lse_part: torch.Tensor, skip_mask: Optional[torch.Tensor], vskip_mask: Optional[torch.Tensor],
-                  Bc: int, lam: float, num_splits: int, causal: bool = True, stream=None) -> None:
-    """q [B,Hq,1,d], k/v [B,Hkv,N,d] bf16; o_part [B,Hq,S,d], lse_part [B,Hq,S] fp32;
-    skip_mask [B,Hq,nk] / vskip_mask [B,Hkv,nk] uint8 or None."""
+def blasst_prefill_ragged(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                          lse: Optional[torch.Tensor], skip_mask: Optional[torch.Tensor], seq_lens: torch.Tensor,
+                          Bc: int, lam: float, causal: bool = True, stream=None) -> None:
+    """As blasst_prefill on padded [B,H,T,d] tensors; seq_lens int32 [B] on the device (rows per sequence)."""
+    B, Hq, T, d, Hkv = _prefill_shapes(q, k, v, o, lse, skip_mask, Bc)
+    _lens(seq_lens, B)
+    st = _load().blasst_prefill_ragged(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(skip_mask),
+                                       _ptr(seq_lens), B, Hq, T, d, Hq // Hkv, Bc, float(lam), int(bool(causal)),
+                                       _stream(stream))
+    _check("blasst_prefill_ragged", st)
+
+
+def _decode_shapes(q, k, v, o_part, lse_part, skip_mask, vskip_mask, Bc, num_splits):
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, nm, torch.bfloat16)
     _need(o_part, "o_part", torch.float32)
@@ -144,10 +169,32 @@ def blasst_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o_part: tor
         _need(vskip_mask, "vskip_mask", torch.uint8)
         if vskip_mask.shape != (B, Hkv, nk):
             raise ValueError("vskip_mask must be [B,Hkv,nk]")
+    return B, Hq, N, d, Hkv
+
+
+def blasst_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o_part: torch.Tensor,
+                  lse_part: torch.Tensor, skip_mask: Optional[torch.Tensor], vskip_mask: Optional[torch.Tensor],
+                  Bc: int, lam: float, num_splits: int, causal: bool = True, stream=None) -> None:
+    """q [B,Hq,1,d], k/v [B,Hkv,N,d] bf16; o_part [B,Hq,S,d], lse_part [B,Hq,S] fp32;
+    skip_mask [B,Hq,nk] / vskip_mask [B,Hkv,nk] uint8 or None."""
+    B, Hq, N, d, Hkv = _decode_shapes(q, k, v, o_part, lse_part, skip_mask, vskip_mask, Bc, num_splits)
     st = _load().blasst_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o_part), _ptr(lse_part), _ptr(skip_mask),
-                               _ptr(vskip_mask), B, Hq, N, d, Hq // Hkv, Bc, float(lam), int(bool(causal)), S,
-                               _stream(stream))
+                               _ptr(vskip_mask), B, Hq, N, d, Hq // Hkv, Bc, float(lam), int(bool(causal)),
+                               num_splits, _stream(stream))
     _check("blasst_decode", st)
+
+
+def blasst_decode_ragged(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o_part: torch.Tensor,
+                         lse_part: torch.Tensor, skip_mask: Optional[torch.Tensor],
+                         vskip_mask: Optional[torch.Tensor], seq_lens: torch.Tensor, Bc: int, lam: float,
+                         num_splits: int, stream=None) -> None:
+    """As blasst_decode on a padded [B,Hkv,N,d] cache; seq_lens int32 [B] on the device (keys per sequence)."""
+    B, Hq, N, d, Hkv = _decode_shapes(q, k, v, o_part, lse_part, skip_mask, vskip_mask, Bc, num_splits)
+    _lens(seq_lens, B)
+    st = _load().blasst_decode_ragged(_ptr(q), _ptr(k), _ptr(v), _ptr(o_part), _ptr(lse_part), _ptr(skip_mask),
+                                      _ptr(vskip_mask), _ptr(seq_lens), B, Hq, N, d, Hq // Hkv, Bc, float(lam),
+                                      num_splits, _stream(stream))
+    _check("blasst_decode_ragged", st)
 
 
 def blasst_decode_combine(o_part: torch.Tensor, lse_part: torch.Tensor, o: torch.Tensor,
@@ -250,6 +297,30 @@ def decode(q, k, v, lam: float, num_splits: int, Bc: int = 128, with_masks: bool
     skip = torch.empty((B, Hq, nk), dtype=torch.uint8, device=q.device) if with_masks else None
     vskip = torch.empty((B, Hkv, nk), dtype=torch.uint8, device=q.device) if with_masks else None
     blasst_decode(q, k, v, o_part, lse_part, skip, vskip, Bc, lam, num_splits)
+    return o_part, lse_part, skip, vskip
+
+
+def prefill_ragged(q, k, v, seq_lens, lam: float, Bc: int = 128, causal: bool = True, with_mask: bool = True):
+    """Allocating wrapper for a ragged batch: returns (o, lse, mask or None) as prefill()."""
+    B, Hq, T, d = q.shape
+    nq = -(-T // Bc)
+    o = torch.empty((B, Hq, T, d), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    mask = torch.empty((B, Hq, nq, nq), dtype=torch.uint8, device=q.device) if with_mask else None
+    blasst_prefill_ragged(q, k, v, o, lse, mask, seq_lens, Bc, lam, causal)
+    return o, lse, mask
+
+
+def decode_ragged(q, k, v, seq_lens, lam: float, num_splits: int, Bc: int = 128, with_masks: bool = True):
+    """Allocating wrapper for a ragged batch: returns (o_part, lse_part, skip, vskip) as decode()."""
+    B, Hq, _, d = q.shape
+    Hkv, N = k.shape[1], k.shape[2]
+    nk = -(-N // Bc)
+    o_part = torch.empty((B, Hq, num_splits, d), dtype=torch.float32, device=q.device)
+    lse_part = torch.empty((B, Hq, num_splits), dtype=torch.float32, device=q.device)
+    skip = torch.empty((B, Hq, nk), dtype=torch.uint8, device=q.device) if with_masks else None
+    vskip = torch.empty((B, Hkv, nk), dtype=torch.uint8, device=q.device) if with_masks else None
+    blasst_decode_ragged(q, k, v, o_part, lse_part, skip, vskip, seq_lens, Bc, lam, num_splits)
     return o_part, lse_part, skip, vskip
 
 

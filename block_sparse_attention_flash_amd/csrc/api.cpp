@@ -30,9 +30,11 @@ blasst_status from_hip(hipError_t e) { return e == hipSuccess ? BLASST_OK : BLAS
 
 }  // namespace
 
-BLASST_EXPORT blasst_status blasst_prefill(const void* q, const void* k, const void* v, float* o, float* lse,
-                                           uint8_t* skip_mask, int B, int Hq, int T, int d, int gqa_ratio,
-                                           int Bc, double lambda, int causal, blasst_stream_t stream) {
+namespace {
+
+blasst_status prefill_impl(const void* q, const void* k, const void* v, float* o, float* lse, uint8_t* skip_mask,
+                           const int32_t* seq_lens, int B, int Hq, int T, int d, int gqa_ratio, int Bc,
+                           double lambda, int causal, blasst_stream_t stream) {
     try {
         if (B < 0 || Hq < 0 || T < 0 || d <= 0 || Bc <= 0 || gqa_ratio < 1) return BLASST_ERR_INVALID_ARG;
         if (Hq % gqa_ratio != 0 || !lambda_ok(lambda) || (causal != 0 && causal != 1))
@@ -61,16 +63,17 @@ BLASST_EXPORT blasst_status blasst_prefill(const void* q, const void* k, const v
         a.causal = causal;
         a.score_scale = static_cast<float>(kLog2e / std::sqrt((double)d));
         a.thr = log2_threshold(lambda);
+        a.lens = seq_lens;
         return from_hip(blasst::launch_prefill(a, d, Bc, reinterpret_cast<hipStream_t>(stream)));
     } catch (...) {
         return BLASST_ERR_INTERNAL;
     }
 }
 
-BLASST_EXPORT blasst_status blasst_decode(const void* q, const void* k, const void* v, float* o_part,
-                                          float* lse_part, uint8_t* skip_mask, uint8_t* vskip_mask, int B,
-                                          int Hq, int N, int d, int gqa_ratio, int Bc, double lambda, int causal,
-                                          int num_splits, blasst_stream_t stream) {
+blasst_status decode_impl(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
+                          uint8_t* skip_mask, uint8_t* vskip_mask, const int32_t* seq_lens, int B, int Hq, int N,
+                          int d, int gqa_ratio, int Bc, double lambda, int causal, int num_splits,
+                          blasst_stream_t stream) {
     try {
         if (B < 0 || Hq < 0 || N <= 0 || d <= 0 || Bc <= 0 || gqa_ratio < 1) return BLASST_ERR_INVALID_ARG;
         if (Hq % gqa_ratio != 0 || !lambda_ok(lambda) || (causal != 0 && causal != 1))
@@ -101,10 +104,46 @@ BLASST_EXPORT blasst_status blasst_decode(const void* q, const void* k, const vo
         a.S = num_splits;
         a.score_scale = static_cast<float>(kLog2e / std::sqrt((double)d));
         a.thr = log2_threshold(lambda);
+        a.lens = seq_lens;
         return from_hip(blasst::launch_decode(a, d, Bc, reinterpret_cast<hipStream_t>(stream)));
     } catch (...) {
         return BLASST_ERR_INTERNAL;
     }
+}
+
+bool lens_ok(const int32_t* seq_lens) { return seq_lens != nullptr && (reinterpret_cast<uintptr_t>(seq_lens) & 3u) == 0; }
+
+}  // namespace
+
+BLASST_EXPORT blasst_status blasst_prefill(const void* q, const void* k, const void* v, float* o, float* lse,
+                                           uint8_t* skip_mask, int B, int Hq, int T, int d, int gqa_ratio,
+                                           int Bc, double lambda, int causal, blasst_stream_t stream) {
+    return prefill_impl(q, k, v, o, lse, skip_mask, nullptr, B, Hq, T, d, gqa_ratio, Bc, lambda, causal, stream);
+}
+
+BLASST_EXPORT blasst_status blasst_prefill_ragged(const void* q, const void* k, const void* v, float* o, float* lse,
+                                                  uint8_t* skip_mask, const int32_t* seq_lens, int B, int Hq, int T,
+                                                  int d, int gqa_ratio, int Bc, double lambda, int causal,
+                                                  blasst_stream_t stream) {
+    if ((int64_t)B * Hq * T != 0 && !lens_ok(seq_lens)) return BLASST_ERR_INVALID_ARG;
+    return prefill_impl(q, k, v, o, lse, skip_mask, seq_lens, B, Hq, T, d, gqa_ratio, Bc, lambda, causal, stream);
+}
+
+BLASST_EXPORT blasst_status blasst_decode(const void* q, const void* k, const void* v, float* o_part,
+                                          float* lse_part, uint8_t* skip_mask, uint8_t* vskip_mask, int B,
+                                          int Hq, int N, int d, int gqa_ratio, int Bc, double lambda, int causal,
+                                          int num_splits, blasst_stream_t stream) {
+    return decode_impl(q, k, v, o_part, lse_part, skip_mask, vskip_mask, nullptr, B, Hq, N, d, gqa_ratio, Bc, lambda,
+                       causal, num_splits, stream);
+}
+
+BLASST_EXPORT blasst_status blasst_decode_ragged(const void* q, const void* k, const void* v, float* o_part,
+                                                 float* lse_part, uint8_t* skip_mask, uint8_t* vskip_mask,
+                                                 const int32_t* seq_lens, int B, int Hq, int N, int d, int gqa_ratio,
+                                                 int Bc, double lambda, int num_splits, blasst_stream_t stream) {
+    if ((int64_t)B * Hq != 0 && !lens_ok(seq_lens)) return BLASST_ERR_INVALID_ARG;
+    return decode_impl(q, k, v, o_part, lse_part, skip_mask, vskip_mask, seq_lens, B, Hq, N, d, gqa_ratio, Bc,
+                       lambda, 1, num_splits, stream);
 }
 
 BLASST_EXPORT blasst_status blasst_decode_combine(const float* o_part, const float* lse_part, float* o, float* lse,

@@ -76,12 +76,27 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
     const int split = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int g = lane >> 4, n = lane & 15;
-    const int N = a.N, nk = a.nk, G = a.G;
+    // Row stride a.N (capacity); this sequence's context is its first N keys, nk
+    // blocks (a ragged batch gives every sequence its own length).  Splits
+    // partition the sequence's own blocks; a split left without one (S > nk)
+    // writes the merge identity, O = 0 and LSE = -inf.
+    const int G = a.G;
+    const int N = a.lens ? __builtin_amdgcn_readfirstlane(min(max(a.lens[b], 0), a.N)) : a.N;
+    const int nk = a.lens ? (N + BC - 1) / BC : a.nk;
     const int j0 = (int)((int64_t)split * nk / a.S);
     const int j1 = (int)((int64_t)(split + 1) * nk / a.S);
 
-    const uint16_t* kbase = a.k + ((size_t)b * a.Hkv + hkv) * (size_t)N * D;
-    const uint16_t* vbase = a.v + ((size_t)b * a.Hkv + hkv) * (size_t)N * D;
+    const uint16_t* kbase = a.k + ((size_t)b * a.Hkv + hkv) * (size_t)a.N * D;
+    const uint16_t* vbase = a.v + ((size_t)b * a.Hkv + hkv) * (size_t)a.N * D;
+    if (a.lens && split == a.S - 1 && nk < a.nk) {
+        // blocks past the sequence's end are not visited (2)
+        for (int x = threadIdx.x; x < (G + 1) * (a.nk - nk); x += 64 * W) {
+            const int r = x / (a.nk - nk), j = nk + x % (a.nk - nk);
+            uint8_t* row = r < G ? a.skip : a.vskip;
+            if (row != nullptr)
+                row[(r < G ? ((size_t)b * a.Hq + (size_t)hkv * G + r) : ((size_t)b * a.Hkv + hkv)) * a.nk + j] = 2;
+        }
+    }
 
     // q^T as the B operand: lane (g, n) holds q[head n][32s + 8g .. +8].
     bf16x8 qf[NT][DS];
@@ -207,7 +222,7 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
                     if constexpr (MARGINS) {
                         const float dm = head_ok[nt] ? (bm - m) * kLn2 : kNegInf;
                         if (wave == 0 && g == 0 && head_ok[nt])
-                            a.margin[((size_t)b * a.Hq + (size_t)hkv * G + nt * 16 + n) * nk + p0 + bi] = dm;
+                            a.margin[((size_t)b * a.Hq + (size_t)hkv * G + nt * 16 + n) * a.nk + p0 + bi] = dm;
                         if (a.vmargin != nullptr) {
                             float vm = dm;
                             vm = fmaxf(vm, __shfl_xor(vm, 1, 64));
@@ -231,7 +246,7 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
         vkeep |= __shfl_xor(vkeep, 8, 64);
         if constexpr (MARGINS) {
             if (a.vmargin != nullptr && wave == 0 && lane == 0) {
-                float* vrow = a.vmargin + ((size_t)b * a.Hkv + hkv) * nk + p0;
+                float* vrow = a.vmargin + ((size_t)b * a.Hkv + hkv) * a.nk + p0;
                 for (int bi = 0; bi < nb; ++bi) vrow[bi] = vmax_blk[bi];
             }
             __syncthreads();  // lds_pmax[parity] is rewritten two phases on
@@ -244,12 +259,12 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
             for (int nt = 0; nt < NT; ++nt) {
                 const int h = nt * 16 + n;
                 if (!head_ok[nt]) continue;
-                uint8_t* row = a.skip + ((size_t)b * a.Hq + (size_t)hkv * G + h) * nk + p0;
+                uint8_t* row = a.skip + ((size_t)b * a.Hq + (size_t)hkv * G + h) * a.nk + p0;
                 for (int bi = wave * 4 + g; bi < nb; bi += 4 * W) row[bi] = (uint8_t)(((keep[nt] >> bi) & 1u) ^ 1u);
             }
         }
         if (a.vskip != nullptr) {
-            uint8_t* row = a.vskip + ((size_t)b * a.Hkv + hkv) * nk + p0;
+            uint8_t* row = a.vskip + ((size_t)b * a.Hkv + hkv) * a.nk + p0;
             for (int bi = threadIdx.x; bi < nb; bi += 64 * W) row[bi] = (uint8_t)(((vkeep >> bi) & 1u) ^ 1u);
         }
 
@@ -349,7 +364,7 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
         const int h = nt * 16 + n;
         if (h < G) {
             const size_t orow = ((size_t)b * a.Hq + (size_t)hkv * G + h) * a.S + split;
-            const float inv = 1.f / lt;
+            const float inv = lt > 0.f ? 1.f / lt : 0.f;  // 0: a split with no block
             for (int dt = wave; dt < DT; dt += W) {
                 float o4[4];
 #pragma unroll
@@ -391,19 +406,24 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restri
         float top = kNegInf;
 #pragma unroll
         for (int s = 0; s < SMAX; ++s) top = fmaxf(top, lv[s]);
+        // every split empty (no key at all): O = 0, LSE = -inf
+        const float ref = top == kNegInf ? 0.f : top;
         float z = 0.f;
 #pragma unroll
-        for (int s = 0; s < SMAX; ++s) z += exp2_fast((lv[s] - top) * kLog2e);
-        total = top + logf(z);
+        for (int s = 0; s < SMAX; ++s) z += exp2_fast((lv[s] - ref) * kLog2e);
+        total = ref + logf(z);
 #pragma unroll
         for (int s = 0; s < SMAX; ++s) acc += exp2_fast((lv[s] - total) * kLog2e) * xv[s];
+        acc = top == kNegInf ? 0.f : acc;
     } else {
         float top = kNegInf;
         for (int s = 0; s < S; ++s) top = fmaxf(top, L[s]);
+        const float ref = top == kNegInf ? 0.f : top;
         float z = 0.f;
-        for (int s = 0; s < S; ++s) z += exp2_fast((L[s] - top) * kLog2e);
-        total = top + logf(z);
+        for (int s = 0; s < S; ++s) z += exp2_fast((L[s] - ref) * kLog2e);
+        total = ref + logf(z);
         for (int s = 0; s < S; ++s) acc += exp2_fast((L[s] - total) * kLog2e) * op[(size_t)s * D];
+        acc = top == kNegInf ? 0.f : acc;
     }
     o[row * D + e] = acc;
     if (e == 0 && lse != nullptr) lse[row] = total;

@@ -20,6 +20,7 @@ struct DecodeArgs {
     float thr;          // ln(lambda) * log2(e); -inf when lambda == 0
     float* margin = nullptr;   // margin pass only: [B, Hq, nk]
     float* vmargin = nullptr;  // margin pass only: [B, Hkv, nk] or null
+    const int* lens = nullptr;  // ragged batch: [B] context lengths (device), clamped to [0, N]; N, nk = capacity
 };
 
 // Causal / full prefill launch.
@@ -34,6 +35,7 @@ struct PrefillArgs {
     float score_scale;
     float thr;
     float* margin = nullptr;  // margin pass only: [B, Hq, nq, nk]
+    const int* lens = nullptr;  // ragged batch: [B] sequence lengths (device), clamped to [0, T]; T, nq = capacity
 };
 
 hipError_t launch_decode(const DecodeArgs& a, int d, int Bc, hipStream_t stream);

@@ -71,7 +71,10 @@ __global__ __launch_bounds__(2 * BC * HPW) void prefill_kernel(PrefillArgs a) {
     int bh = L % bh_count;
     if (bh_count % 8 == 0) bh = (bh % 8) * (bh_count / 8) + bh / 8;
     const int hgrp = bh % hg_count, b = bh / hg_count;
-    const int T = a.T;
+    // Row stride Tcap; this sequence holds its first T rows (a ragged batch
+    // gives every sequence its own length, a plain one T = Tcap).
+    const int Tcap = a.T;
+    const int T = a.lens ? __builtin_amdgcn_readfirstlane(min(max(a.lens[b], 0), Tcap)) : Tcap;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -81,21 +84,36 @@ __global__ __launch_bounds__(2 * BC * HPW) void prefill_kernel(PrefillArgs a) {
     const int col = lane & 31, half = lane >> 5;   // query column of S^T / O^T, and lane half
     const int qidx = i * BC + 32 * wrow + col;     // this lane's query row
     const bool row_ok = qidx < T;
+    uint8_t* mask_row = a.mask ? a.mask + (((size_t)b * a.Hq + hq) * a.nq + i) * a.nk : nullptr;
 
-    const uint16_t* kbase = a.k + ((size_t)b * a.Hkv + hkv) * (size_t)T * D;
-    const uint16_t* vbase = a.v + ((size_t)b * a.Hkv + hkv) * (size_t)T * D;
+    if (i * BC >= T) {
+        // a query block past the end of its sequence: padded rows hold O = 0 and
+        // LSE = -inf, and no tile of the row is visited
+        if (qidx < Tcap) {
+            float* orow = a.o + (((size_t)b * a.Hq + hq) * Tcap + qidx) * D;
+#pragma unroll
+            for (int e = 0; e < D / 2; e += 4) *(f32x4*)(orow + e + (D / 2) * half) = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (half == 0 && a.lse) a.lse[((size_t)b * a.Hq + hq) * Tcap + qidx] = kNegInf;
+        }
+        if (mask_row && wrow == 0)
+            for (int j = lane; j < a.nk; j += 64) mask_row[j] = 2;
+        return;
+    }
+
+    const uint16_t* kbase = a.k + ((size_t)b * a.Hkv + hkv) * (size_t)Tcap * D;
+    const uint16_t* vbase = a.v + ((size_t)b * a.Hkv + hkv) * (size_t)Tcap * D;
     const float c = a.score_scale;
 
     // Q^T as the B operand: lane holds q[qidx][16s + 8*half .. +8].
     bf16x8 qf[DS];
     {
-        const uint16_t* qrow = a.q + (((size_t)b * a.Hq + hq) * T + min(qidx, T - 1)) * D;
+        const uint16_t* qrow = a.q + (((size_t)b * a.Hq + hq) * Tcap + min(qidx, T - 1)) * D;
 #pragma unroll
         for (int s = 0; s < DS; ++s) qf[s] = as_bf16x8(load16(qrow + 16 * s + 8 * half));
     }
 
     const int last_row = min(T, (i + 1) * BC) - 1;
-    const int jend = a.causal ? last_row / BC + 1 : a.nk;
+    const int jend = a.causal ? last_row / BC + 1 : (T + BC - 1) / BC;
 
     f32x16 oacc[DT];
 #pragma unroll
@@ -144,8 +162,6 @@ __global__ __launch_bounds__(2 * BC * HPW) void prefill_kernel(PrefillArgs a) {
     }
     static_assert(CPR == 8 || CPR == 16, "swizzle offsets assume 8 or 16 chunks per row");
     constexpr int VH8 = (chunk_swizzle<CPR>(8) ^ chunk_swizzle<CPR>(0)) << 4;
-
-    uint8_t* mask_row = a.mask ? a.mask + (((size_t)b * a.Hq + hq) * a.nq + i) * a.nk : nullptr;
 
     // ---- phase X_j: S^T(j) = K(j) Q^T, row max, this wave's vote (state kept for Y_j)
     f32x16 sacc[KT];
@@ -329,9 +345,10 @@ __global__ __launch_bounds__(2 * BC * HPW) void prefill_kernel(PrefillArgs a) {
 
     // ---- epilogue: O / l and LSE for this lane's row
     l += wave_shfl_xor(l, 32);
-    if (row_ok) {
-        const float inv = 1.f / l;
-        float* orow = a.o + (((size_t)b * a.Hq + hq) * T + qidx) * D;
+    if (qidx < Tcap) {
+        // rows past a ragged sequence's end (inside its last block) hold O = 0, LSE = -inf
+        const float inv = row_ok ? 1.f / l : 0.f;
+        float* orow = a.o + (((size_t)b * a.Hq + hq) * Tcap + qidx) * D;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -339,7 +356,7 @@ __global__ __launch_bounds__(2 * BC * HPW) void prefill_kernel(PrefillArgs a) {
                 *(f32x4*)(orow + 32 * dt + 8 * eg + 4 * half) =
                     f32x4{oacc[dt][4 * eg] * inv, oacc[dt][4 * eg + 1] * inv, oacc[dt][4 * eg + 2] * inv,
                           oacc[dt][4 * eg + 3] * inv};
-        if (half == 0 && a.lse) a.lse[((size_t)b * a.Hq + hq) * T + qidx] = m * c * kLn2 + logf(l);
+        if (half == 0 && a.lse) a.lse[((size_t)b * a.Hq + hq) * Tcap + qidx] = row_ok ? m * c * kLn2 + logf(l) : kNegInf;
     }
     if (mask_row && wrow == 0)
         for (int j = jend + lane; j < a.nk; j += 64) mask_row[j] = 2;

@@ -33,7 +33,8 @@
  *     rejected call enqueues nothing.  A launch failure returns BLASST_ERR_HIP.
  *     No C++ exception crosses this interface.
  *   - Mask bytes: 0 = block kept, 1 = block skipped, 2 = block not visited
- *     (prefill, above the causal diagonal).
+ *     (prefill, above the causal diagonal; ragged batches, past a sequence's
+ *     end).
  */
 #ifndef BLASST_H
 #define BLASST_H
@@ -110,8 +111,46 @@ blasst_status blasst_decode(const void* q, const void* k, const void* v, float* 
                             int causal, int num_splits, blasst_stream_t stream);
 
 /*
+ * Ragged batches: one length per sequence (the serving-shaped form of the same
+ * two calls).  The tensors keep their padded layout -- T (prefill) or N
+ * (decode) is the capacity, the row stride of every sequence -- and sequence b
+ * uses only its first seq_lens[b] rows, each sequence being exactly the
+ * plain call at its own length.
+ *
+ *   seq_lens  int32 [B], device memory, 4-byte aligned; values are clamped to
+ *             [0, T] or [0, N] on the device (they are never read on the host).
+ *
+ * blasst_prefill_ragged: arguments as blasst_prefill.  Sequence b is a causal
+ * (or full) prefill of its first L_b = seq_lens[b] query rows over its first L_b
+ * keys.  Rows t >= L_b hold O = 0 and LSE = -inf; skip_mask entries of query
+ * blocks i >= ceil(L_b/Bc) and of KV blocks j >= ceil(L_b/Bc) are 2 (not visited).
+ * Errors as blasst_prefill, plus INVALID_ARG for a null or misaligned seq_lens
+ * when B*Hq*T != 0.
+ */
+blasst_status blasst_prefill_ragged(const void* q, const void* k, const void* v, float* o, float* lse,
+                                    uint8_t* skip_mask, const int32_t* seq_lens, int B, int Hq, int T, int d,
+                                    int gqa_ratio, int Bc, double lambda, int causal, blasst_stream_t stream);
+
+/*
+ * blasst_decode_ragged: arguments as blasst_decode (without `causal`).
+ * Sequence b attends to its first N_b = seq_lens[b] keys; its nk_b =
+ * ceil(N_b/Bc) blocks are cut into the num_splits ranges of blasst_decode.  A
+ * split left with no block (num_splits > nk_b, or N_b = 0) writes O = 0 and
+ * LSE = -inf, the identity of the merge.  Mask entries of blocks j >= nk_b are
+ * 2 (not visited).  num_splits is checked against the capacity:
+ * 1 <= num_splits <= ceil(N/Bc).  Errors as blasst_decode, plus INVALID_ARG for
+ * a null or misaligned seq_lens when B*Hq != 0.
+ */
+blasst_status blasst_decode_ragged(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
+                                   uint8_t* skip_mask, uint8_t* vskip_mask, const int32_t* seq_lens, int B, int Hq,
+                                   int N, int d, int gqa_ratio, int Bc, double lambda, int num_splits,
+                                   blasst_stream_t stream);
+
+/*
  * Merge of the splits by their true normalisers (SANTA notes, merge of
  * FlashDecoding tiles): LSE = ln sum_s exp(lse_s), O = sum_s exp(lse_s - LSE) O_s.
+ * A split with lse_s = -inf contributes nothing; when every split has
+ * lse_s = -inf (no key at all) the row gets O = 0 and LSE = -inf.
  *
  *   o_part     fp32 [B, Hq, num_splits, d]
  *   lse_part   fp32 [B, Hq, num_splits]

@@ -27,8 +27,8 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert declared() == ["blasst_decode", "blasst_decode_combine", "blasst_decode_margins", "blasst_prefill",
-                          "blasst_prefill_margins", "blasst_status_string"]
+    assert declared() == ["blasst_decode", "blasst_decode_combine", "blasst_decode_margins", "blasst_decode_ragged",
+                          "blasst_prefill", "blasst_prefill_margins", "blasst_prefill_ragged", "blasst_status_string"]
 
 
 def test_exports_match_header(lib):
@@ -118,3 +118,32 @@ def test_prefill_margins_validation(lib, kw, status):
 ])
 def test_decode_margins_validation(lib, kw, status):
     assert decode_margins(lib, **kw) == status
+
+
+def prefill_ragged(lib, lens=FAKE, q=FAKE, B=2, Hq=4, T=256, d=128, G=4, Bc=128, lam=1e-3, causal=1):
+    f = lib.blasst_prefill_ragged
+    f.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, D, I, P]
+    return f(q, FAKE, FAKE, FAKE, None, None, lens, B, Hq, T, d, G, Bc, lam, causal, None)
+
+
+def decode_ragged(lib, lens=FAKE, q=FAKE, B=2, Hq=4, N=256, d=128, G=4, Bc=128, lam=1e-3, S=2):
+    f = lib.blasst_decode_ragged
+    f.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, D, I, P]
+    return f(q, FAKE, FAKE, FAKE, FAKE, None, None, lens, B, Hq, N, d, G, Bc, lam, S, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(lens=None), 1), (dict(lens=P(0x1002)), 1), (dict(q=None), 1), (dict(T=-1), 1), (dict(G=3), 1),
+    (dict(lam=1.0), 1), (dict(causal=2), 1), (dict(d=96), 2), (dict(B=0, lens=None), 0), (dict(T=0, lens=None), 0),
+])
+def test_prefill_ragged_validation(lib, kw, status):
+    assert prefill_ragged(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(lens=None), 1), (dict(lens=P(0x1001)), 1), (dict(q=None), 1), (dict(N=0), 1), (dict(S=3), 1),
+    (dict(S=0), 1), (dict(lam=-1.0), 1), (dict(Bc=256, S=1), 2), (dict(Hq=128, G=128), 2),
+    (dict(B=0, lens=None), 0),
+])
+def test_decode_ragged_validation(lib, kw, status):
+    assert decode_ragged(lib, **kw) == status
