@@ -193,8 +193,15 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
                     }
                     t[u][kt][nt] = acc;
                 }
-                pm = fmaxf(pm, wave_shfl_xor(pm, 16));
-                pm = fmaxf(pm, wave_shfl_xor(pm, 32));
+                // over the 4 lane groups g (the 16 key rows of each): the permlane
+                // form is faster but takes two registers, which one head tile's
+                // ring-fed K pass cannot spare
+                if constexpr (NT == 1) {
+                    pm = fmaxf(pm, wave_shfl_xor(pm, 16));
+                    pm = fmaxf(pm, wave_shfl_xor(pm, 32));
+                } else {
+                    pm = wave_max_xor32(wave_max_xor16(pm));
+                }
                 if (uok[u] && g == 0) lds_pmax[parity][(wave + W * u) * HT + nt * 16 + n] = pm;
             }
         }
@@ -209,27 +216,33 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
         for (int bi = 0; bi < (MARGINS ? BPP : 1); ++bi) vmax_blk[bi] = kNegInf;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
+            // block maxima four blocks at a time: each group's LDS reads go out together
             float m = m_run[nt];
             uint32_t kb = 0;
+            constexpr int BG = BPP < 4 ? BPP : 4;
 #pragma unroll
-            for (int bi = 0; bi < BPP; ++bi) {
-                if (bi < nb) {
+            for (int b0 = 0; b0 < BPP; b0 += BG) {
+                float bmv[BG];
+#pragma unroll
+                for (int bb = 0; bb < BG; ++bb) {
                     float bm = kNegInf;
 #pragma unroll
-                    for (int kg = 0; kg < KG; ++kg) bm = fmaxf(bm, lds_pmax[parity][(bi * KG + kg) * HT + nt * 16 + n]);
-                    m = fmaxf(m, bm);
-                    kb |= (uint32_t)(!((bm - m) < a.thr)) << bi;
-                    if constexpr (MARGINS) {
-                        const float dm = head_ok[nt] ? (bm - m) * kLn2 : kNegInf;
-                        if (wave == 0 && g == 0 && head_ok[nt])
-                            a.margin[((size_t)b * a.Hq + (size_t)hkv * G + nt * 16 + n) * a.nk + p0 + bi] = dm;
-                        if (a.vmargin != nullptr) {
-                            float vm = dm;
-                            vm = fmaxf(vm, __shfl_xor(vm, 1, 64));
-                            vm = fmaxf(vm, __shfl_xor(vm, 2, 64));
-                            vm = fmaxf(vm, __shfl_xor(vm, 4, 64));
-                            vm = fmaxf(vm, __shfl_xor(vm, 8, 64));
-                            vmax_blk[bi] = fmaxf(vmax_blk[bi], vm);
+                    for (int kg = 0; kg < KG; ++kg)
+                        bm = fmaxf(bm, lds_pmax[parity][((b0 + bb) * KG + kg) * HT + nt * 16 + n]);
+                    bmv[bb] = bm;
+                }
+#pragma unroll
+                for (int bb = 0; bb < BG; ++bb) {
+                    const int bi = b0 + bb;
+                    if (bi < nb) {
+                        const float bm = bmv[bb];
+                        m = fmaxf(m, bm);
+                        kb |= (uint32_t)(!((bm - m) < a.thr)) << bi;
+                        if constexpr (MARGINS) {
+                            const float dm = head_ok[nt] ? (bm - m) * kLn2 : kNegInf;
+                            if (wave == 0 && g == 0 && head_ok[nt])
+                                a.margin[((size_t)b * a.Hq + (size_t)hkv * G + nt * 16 + n) * a.nk + p0 + bi] = dm;
+                            if (a.vmargin != nullptr) vmax_blk[bi] = fmaxf(vmax_blk[bi], row16_max(dm));
                         }
                     }
                 }
@@ -240,10 +253,7 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
             alpha[nt] = head_ok[nt] ? exp2_fast(m_run[nt] - m) : 1.f;
             m_run[nt] = head_ok[nt] ? m : m_run[nt];
         }
-        vkeep |= __shfl_xor(vkeep, 1, 64);
-        vkeep |= __shfl_xor(vkeep, 2, 64);
-        vkeep |= __shfl_xor(vkeep, 4, 64);
-        vkeep |= __shfl_xor(vkeep, 8, 64);
+        vkeep = row16_or(vkeep);
         if constexpr (MARGINS) {
             if (a.vmargin != nullptr && wave == 0 && lane == 0) {
                 float* vrow = a.vmargin + ((size_t)b * a.Hkv + hkv) * a.nk + p0;
@@ -349,9 +359,7 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
     float* red = (float*)lds_v;  // [W waves][DT][4][64]
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-        float l = l_part[nt];
-        l += wave_shfl_xor(l, 16);
-        l += wave_shfl_xor(l, 32);
+        const float l = wave_sum_xor32(wave_sum_xor16(l_part[nt]));
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll

@@ -122,4 +122,53 @@ __device__ __forceinline__ float wave_shfl_xor(float x, int mask) {
     return __shfl_xor(x, mask, 64);
 }
 
+// Cross-lane reductions on the VALU (no LDS round trip).  gfx950's
+// v_permlane32_swap applied to (x, x) leaves x of lane (i & 31) in the first
+// result and x of lane 32 + (i & 31) in the second; v_permlane16_swap does the
+// same for the 16-lane rows of each half (rows 0/2 and 1/3).  Combining the two
+// results reduces over lanes i and i ^ 32 (resp. i ^ 16) in every lane.  The
+// DPP forms reduce within a 16-lane row: quad_perm [1,0,3,2] and [2,3,0,1]
+// pair lanes i ^ 1 and i ^ 2, then row_half_mirror (i <-> 7 - i within 8
+// lanes) and row_mirror (i <-> 15 - i) join the quads and the half rows.
+// (Lane layouts verified on the device.)
+__device__ __forceinline__ float wave_max_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const uint32_t a = r[0], b = r[1];
+    return fmaxf(__uint_as_float(a), __uint_as_float(b));
+}
+__device__ __forceinline__ float wave_sum_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const uint32_t a = r[0], b = r[1];
+    return __uint_as_float(a) + __uint_as_float(b);
+}
+__device__ __forceinline__ float wave_max_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const uint32_t a = r[0], b = r[1];
+    return fmaxf(__uint_as_float(a), __uint_as_float(b));
+}
+__device__ __forceinline__ float wave_sum_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const uint32_t a = r[0], b = r[1];
+    return __uint_as_float(a) + __uint_as_float(b);
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, false);
+}
+// OR / max over the 16 lanes of each row (every lane gets its row's result)
+__device__ __forceinline__ uint32_t row16_or(uint32_t x) {
+    x |= dpp_u32<0xB1>(x);   // quad_perm [1,0,3,2]
+    x |= dpp_u32<0x4E>(x);   // quad_perm [2,3,0,1]
+    x |= dpp_u32<0x141>(x);  // row_half_mirror
+    x |= dpp_u32<0x140>(x);  // row_mirror
+    return x;
+}
+__device__ __forceinline__ float row16_max(float x) {
+    x = fmaxf(x, __uint_as_float(dpp_u32<0xB1>(__float_as_uint(x))));
+    x = fmaxf(x, __uint_as_float(dpp_u32<0x4E>(__float_as_uint(x))));
+    x = fmaxf(x, __uint_as_float(dpp_u32<0x141>(__float_as_uint(x))));
+    x = fmaxf(x, __uint_as_float(dpp_u32<0x140>(__float_as_uint(x))));
+    return x;
+}
+
 }  // namespace blasst

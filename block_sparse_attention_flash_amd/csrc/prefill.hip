@@ -217,7 +217,7 @@ __global__ __launch_bounds__(2 * BC * HPW) void prefill_kernel(PrefillArgs a) {
         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
             for (int e = 0; e < 16; ++e) mt = fmaxf(mt, sacc[kt][e]);
-        mt = fmaxf(mt, wave_shfl_xor(mt, 32));
+        mt = wave_max_xor32(mt);
         // Eq. 1 then the log-space test (log2 units)
         m_new = fmaxf(m, mt);
         const bool vote_skip = !row_ok || mt == kNegInf || (mt - m_new) * c < a.thr;
@@ -344,7 +344,7 @@ __global__ __launch_bounds__(2 * BC * HPW) void prefill_kernel(PrefillArgs a) {
     }
 
     // ---- epilogue: O / l and LSE for this lane's row
-    l += wave_shfl_xor(l, 32);
+    l = wave_sum_xor32(l);
     if (qidx < Tcap) {
         // rows past a ragged sequence's end (inside its last block) hold O = 0, LSE = -inf
         const float inv = row_ok ? 1.f / l : 0.f;
@@ -499,13 +499,12 @@ __global__ __launch_bounds__(2 * BC) void prefill_margin_kernel(PrefillArgs a) {
         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
             for (int e = 0; e < 16; ++e) mt = fmaxf(mt, sacc[kt][e]);
-        mt = fmaxf(mt, wave_shfl_xor(mt, 32));
+        mt = wave_max_xor32(mt);
         const float m_new = fmaxf(m, mt);
         // a row that sees no key of the tile, or a row past T, votes skip with no effect
         float dr = (row_ok && mt != kNegInf) ? (mt - m_new) * inv_sqrt_d : kNegInf;
         m = m_new;
-#pragma unroll
-        for (int sh = 1; sh < 64; sh <<= 1) dr = fmaxf(dr, wave_shfl_xor(dr, sh));
+        dr = wave_max_xor32(wave_max_xor16(row16_max(dr)));
         if (lane == 0) lds_m[j & 1][wave] = dr;
     }
     __syncthreads();
