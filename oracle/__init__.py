@@ -48,6 +48,8 @@ def _load():
         lib.oracle_decode.restype = i
         lib.oracle_combine.argtypes = [P, P, i, i, i, P, P]
         lib.oracle_combine.restype = i
+        lib.oracle_decode_mla.argtypes = [P, P, i, i, i, i, i, i, dbl, dbl, i, P, i, P, P, P, P, P, i]
+        lib.oracle_decode_mla.restype = i
         _lib = lib
     return _lib
 
@@ -198,6 +200,47 @@ def decode_ragged(q, k, v, lens, Bc: int, lam: float, num_splits: int,
         skip[b, :, :n] = r["skip_full"][0]
         vskip[b, :, :n] = r["vskip_full"][0]
     return dict(o_part_full=o_part, lse_part_full=lse_part, skip_full=skip, vskip_full=vskip)
+
+
+def decode_mla(q, kv, Bc: int, lam: float, num_splits: int, scale: float, dv: int,
+               units: Optional[Sequence[int]] = None, force: Optional[np.ndarray] = None,
+               threads: Optional[int] = None) -> dict:
+    """MLA decode (absorbed latent form).  q [B,Hq,dqk] (or [B,Hq,1,dqk]), kv [B,N,dqk]
+    (bf16 bits); token t's value is kv[..., t, :dv]; scores are (q . kv_t) * scale.
+
+    units: (b, h) units b*Hq + h (default: all).  Returns per-unit o_part [U,S,dv],
+    lse_part [U,S], skip [U,nk], margin [U,nk] (skipped iff < 0); with all units also
+    o_part_full [B,Hq,S,dv], lse_part_full [B,Hq,S], skip_full [B,Hq,nk], and
+    vskip_full [B,nk] / vmargin_full [B,nk]: no head kept the block (its P V is not
+    formed for any head) iff vmargin < 0.
+    """
+    q, kv = _u16(q), _u16(kv)
+    B, Hq, dqk = q.shape[0], q.shape[1], q.shape[-1]
+    N = kv.shape[1]
+    if q.size != B * Hq * dqk or kv.shape != (B, N, dqk):
+        raise ValueError("q must be [B,Hq,dqk] and kv [B,N,dqk]")
+    S, nk = num_splits, -(-N // Bc)
+    all_units = units is None
+    units = np.arange(B * Hq, dtype=np.int64) if all_units else np.asarray(units, np.int64)
+    U = len(units)
+    o_part = np.full((U, S, dv), np.nan)
+    lse_part = np.full((U, S), np.nan)
+    skip = np.empty((U, nk), np.uint8)
+    margin = np.empty((U, nk))
+    f = None if force is None else np.ascontiguousarray(force, np.int8).reshape(U, nk)
+    rc = _load().oracle_decode_mla(_ptr(q), _ptr(kv), B, Hq, N, dqk, dv, Bc, float(scale), float(lam), S,
+                                   _ptr(units), U, _ptr(f), _ptr(o_part), _ptr(lse_part), _ptr(skip), _ptr(margin),
+                                   _threads(threads))
+    if rc:
+        raise ValueError("oracle_decode_mla rejected its arguments")
+    out = dict(o_part=o_part, lse_part=lse_part, skip=skip, margin=margin, units=units)
+    if all_units:
+        out["o_part_full"] = o_part.reshape(B, Hq, S, dv)
+        out["lse_part_full"] = lse_part.reshape(B, Hq, S)
+        out["skip_full"] = skip.reshape(B, Hq, nk)
+        out["vskip_full"] = skip.reshape(B, Hq, nk).min(axis=1)
+        out["vmargin_full"] = margin.reshape(B, Hq, nk).max(axis=1)
+    return out
 
 
 def combine(o_part: np.ndarray, lse_part: np.ndarray):

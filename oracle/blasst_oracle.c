@@ -326,6 +326,90 @@ int oracle_decode(const uint16_t* q, const uint16_t* k, const uint16_t* v,
     return 0;
 }
 
+/* ------------------------------------------------------------------------ */
+/* MLA decode (latent KV, absorbed form)                                     */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * One query head of multi-head latent attention at decode: every head of
+ * sequence b reads the same cache row per token, kv [N, dqk] (the latent part
+ * followed by the rotary part), and token t's value is the latent part
+ * kv_t[0 .. dv).  Scores s_t = (q . kv_t) * scale.  Blocks, splits, decisions
+ * and the kept-block update are those of split-KV decode; the head decides
+ * alone.  unit = b*Hq + h.  Per-unit outputs:
+ *   o_part [S, dv], lse_part [S], skip [nk], margin [nk] (D - ln(lambda)).
+ * force (nullable) [nk]: -1 = own decision, 0 = keep, 1 = skip.
+ */
+static void mla_unit(const uint16_t* q, const uint16_t* kv, int Hq, int N, int dqk, int dv, int Bc,
+                     double scale, double thr, int S, int64_t unit, const int8_t* force,
+                     double* o_part, double* lse_part, uint8_t* skip, double* margin)
+{
+    const int nk = ceil_div(N, Bc);
+    const int64_t b = unit / Hq;
+    const uint16_t* K = kv + (size_t)b * N * dqk;
+
+    double* qd = malloc(sizeof(double) * dqk);
+    double* kb = malloc(sizeof(double) * (size_t)Bc * dqk);
+    double* vb = malloc(sizeof(double) * (size_t)Bc * dv);
+    double* s = malloc(sizeof(double) * Bc);
+    double* acc = malloc(sizeof(double) * dv);
+    widen(q + (size_t)unit * dqk, qd, dqk);
+    for (int sp = 0; sp < S; ++sp) {
+        const int j0 = (int)((int64_t)sp * nk / S), j1 = (int)((int64_t)(sp + 1) * nk / S);
+        double m = -INFINITY, l = 0.0;
+        for (int e = 0; e < dv; ++e) acc[e] = 0.0;
+        for (int j = j0; j < j1; ++j) {
+            const int c0 = j * Bc, nc = (N - c0 < Bc) ? N - c0 : Bc;
+            widen(K + (size_t)c0 * dqk, kb, (size_t)nc * dqk);
+            double row_max = -INFINITY;
+            for (int c = 0; c < nc; ++c) {
+                double dot = 0.0;
+                for (int e = 0; e < dqk; ++e) dot += qd[e] * kb[(size_t)c * dqk + e];
+                s[c] = dot * scale;
+                if (s[c] > row_max) row_max = s[c];
+            }
+            double m_new = (m > row_max) ? m : row_max;
+            double diff = row_max - m_new;
+            int sk = diff < thr;
+            if (force && force[j] >= 0) sk = force[j];
+            skip[j] = (uint8_t)sk;
+            margin[j] = (thr == -INFINITY) ? INFINITY : diff - thr;
+            if (sk) continue;
+            /* the value of a token is the latent part of its cache row */
+            for (int c = 0; c < nc; ++c)
+                for (int e = 0; e < dv; ++e) vb[(size_t)c * dv + e] = kb[(size_t)c * dqk + e];
+            accumulate_kept_block(&m, &l, acc, s, vb, nc, dv, m_new);
+        }
+        for (int e = 0; e < dv; ++e) o_part[(size_t)sp * dv + e] = (j1 > j0) ? acc[e] / l : 0.0;
+        lse_part[sp] = (j1 > j0) ? m + log(l) : -INFINITY;
+    }
+    free(qd); free(kb); free(vb); free(s); free(acc);
+}
+
+/*
+ * MLA decode over a list of (b, h) units; q [B,Hq,dqk], kv [B,N,dqk], value =
+ * kv[..., :dv].  Returns 0, or -1 on a bad argument.
+ */
+int oracle_decode_mla(const uint16_t* q, const uint16_t* kv, int B, int Hq, int N, int dqk, int dv, int Bc,
+                      double scale, double lambda, int num_splits, const int64_t* units, int n_units,
+                      const int8_t* force, double* o_part, double* lse_part, uint8_t* skip, double* margin,
+                      int nthreads)
+{
+    if (B < 0 || Hq <= 0 || N < 0 || dqk <= 0 || dv <= 0 || dv > dqk || Bc <= 0 || num_splits < 1) return -1;
+    if (!(lambda >= 0.0 && lambda < 1.0) || !(scale > 0.0)) return -1;
+    const int nk = ceil_div(N, Bc), S = num_splits;
+    const double thr = log_threshold(lambda);
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+    for (int u = 0; u < n_units; ++u)
+        mla_unit(q, kv, Hq, N, dqk, dv, Bc, scale, thr, S, units[u], force ? force + (size_t)u * nk : NULL,
+                 o_part + (size_t)u * S * dv, lse_part + (size_t)u * S, skip + (size_t)u * nk,
+                 margin + (size_t)u * nk);
+    return 0;
+}
+
 /*
  * Merge of split results by their true normalisers: with L = ln(sum_s exp(lse_s)),
  * O = sum_s exp(lse_s - L) O_s.  o_part [rows, S, d], lse_part [rows, S];

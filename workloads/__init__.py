@@ -19,6 +19,9 @@ the generator reproduces that shape with a planted direction:
   over an N(0, 1 + a^2/d) background.
 * optionally the last `window` keys get + c_w*u with c_w = window_logit*sqrt(d)/a,
   i.e. a recent-window bias of +window_logit in the scaled logit.
+* the score scale is 1/sqrt(d) unless a workload sets another (MLA: the
+  model's scale over d = 576 cache columns); amplitudes are set so that the
+  scaled logits above hold at that scale.
 * optionally (logit_tail = tau > 0) every key j gets + e_j*sqrt(d)/a * u with
   e_j ~ Exponential(mean tau): an extra scaled logit of about e_j, so that the
   scores have an exponential upper tail and the running max of a row grows like
@@ -67,6 +70,8 @@ class Workload:
     hot_logit: float = 8.0
     num_splits: int = 1  # decode only
     logit_tail: float = 0.0  # mean of the exponential extra logit per key (0: off)
+    dv: int = 0              # MLA: value width (the first dv columns of a cache row); 0: not MLA
+    scale: float = 0.0       # softmax scale of the scores; 0: 1/sqrt(d)
 
     @property
     def G(self) -> int:
@@ -77,13 +82,17 @@ class Workload:
         return self.T if self.kind == "prefill" else 1
 
     @property
+    def score_scale(self) -> float:
+        return self.scale if self.scale > 0 else 1.0 / math.sqrt(self.d)
+
+    @property
     def amplitude(self) -> float:
-        # hot logit = a^2 / sqrt(d)
-        return math.sqrt(self.hot_logit * math.sqrt(self.d))
+        # hot logit = a^2 * scale (a^2 / sqrt(d) at the default scale)
+        return math.sqrt(self.hot_logit / self.score_scale)
 
     @property
     def window_coef(self) -> float:
-        return self.window_logit * math.sqrt(self.d) / self.amplitude
+        return self.window_logit / (self.score_scale * self.amplitude)
 
     def with_(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -108,6 +117,15 @@ CONFIGS = {
     "decode_mqa_16k": Workload("decode_mqa_16k", "decode", B=64, Hq=64, Hkv=1, d=128, T=16384,
                                Bc=128, lambdas=(1e-3,), hot_rate=0.02, seed=_seed(5),
                                num_splits=8),
+}
+
+# MLA decode (DeepSeek-V3-like absorbed attention: 128 heads over 512 latent +
+# 64 rotary columns, softmax scale 1/sqrt(128 + 64)); the cache is the "k"
+# tensor with one kv head, the value is its first dv columns.
+MLA_CONFIGS = {
+    "decode_mla_32k": Workload("decode_mla_32k", "decode", B=8, Hq=128, Hkv=1, d=576, T=32768, Bc=64,
+                               lambdas=(1e-3,), hot_rate=0.01, seed=_seed(8), window=512, num_splits=16,
+                               dv=512, scale=1.0 / math.sqrt(192.0)),
 }
 
 
@@ -186,7 +204,7 @@ def k_slice(w: Workload, b: int, hkv: int) -> np.ndarray:
         x[max(0, w.T - w.window):] += np.float32(w.window_coef) * u
     if w.logit_tail > 0:
         e = _rng(w, _TAG_TAIL, b, hkv).exponential(w.logit_tail, size=w.T).astype(np.float32)
-        x += (e * np.float32(math.sqrt(w.d) / w.amplitude))[:, None] * u[None, :]
+        x += (e * np.float32(1.0 / (w.score_scale * w.amplitude)))[:, None] * u[None, :]
     return to_bf16_bits(x)
 
 
