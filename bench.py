@@ -13,7 +13,9 @@ decision bytes, divided by the step time), plus the decode split kernel's
 roofline (its algorithmic bytes per launch over its average launch duration
 from HIP events on the launch stream), the 32K causal prefill's executed
 TFLOP/s at lambda in {1e-4, 1e-3, 1e-2} and the dense (lambda = 0) reference,
-block sparsity, and the FP64 oracle timed on this host as a CPU baseline.
+block sparsity, the MLA decode kernel at 32K context (128 heads, 576-column latent
+cache) against its HBM and MFMA rooflines, and the FP64 oracle timed on this host
+as a CPU baseline.
 """
 from __future__ import annotations
 
@@ -77,6 +79,7 @@ def parse():
     p.add_argument("--copies", type=int, default=4, help="KV copies rotated to defeat the Infinity Cache")
     p.add_argument("--prefill-reps", type=int, default=5)
     p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--no-mla", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--profile-target", choices=["decode", "prefill", "copy"], default=None,
@@ -335,6 +338,60 @@ def bench_prefill(args, lib, torch, W):
                 hbm_traffic_bytes_per_launch=measured_traffic("prefill_kernel", w.name))
 
 
+def bench_mla(args, lib, torch, W):
+    """MLA decode split kernel at 32K context: time, HBM bytes (the cache rows are read once), the
+    executed FLOPs (S for every head and token; P V for the kept blocks of each head group) and the
+    roofline bound by both HBM and MFMA."""
+    w = W.MLA_CONFIGS["decode_mla_32k"]
+    x = W.generate(w, parts=("q", "k"))
+    q = dev(np.ascontiguousarray(x["q"][:, :, 0]))
+    kvs = [dev(np.ascontiguousarray(x["k"][:, 0]))]
+    kvs.append(kvs[0].clone())  # two copies, 604 MB: beyond the Infinity Cache
+    del x
+    B, Hq, N, dqk, dv, Bc, S = w.B, w.Hq, w.T, w.d, w.dv, w.Bc, w.num_splits
+    nk = -(-N // Bc)
+    o_part = torch.empty((B, Hq, S, dv), dtype=torch.float32, device="cuda")
+    lse_part = torch.empty((B, Hq, S), dtype=torch.float32, device="cuda")
+    skip = torch.empty((B, Hq, nk), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    hg = 64 if (Hq % 64 == 0 and S * (Hq // 64) * B >= 256) else 32
+    out = {}
+    for lam in (0.0,) + tuple(w.lambdas):
+        args_ = [(P(q), P(kv), P(o_part), P(lse_part), P(skip), B, Hq, N, dqk, dv, Bc, ctypes.c_double(w.score_scale),
+                  ctypes.c_double(lam), S, ctypes.c_void_p(stream.cuda_stream)) for kv in kvs]
+        for i in range(4):
+            assert lib.blasst_decode_mla(*args_[i % 2]) == 0
+        torch.cuda.synchronize()
+        reps = 50
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        for i in range(reps):
+            assert lib.blasst_decode_mla(*args_[i % 2]) == 0
+        s1.record(stream)
+        torch.cuda.synchronize()
+        us = s0.elapsed_time(s1) * 1e3 / reps
+        sk = skip.cpu().numpy().astype(bool)                      # [B, Hq, nk]
+        group_kept = ~sk.reshape(B, Hq // hg, hg, nk).all(axis=2)  # P V formed for the group
+        rows = np.minimum(Bc, N - Bc * np.arange(nk))              # tokens per block
+        s_flops = 2.0 * dqk * N * Hq * B
+        pv_flops = 2.0 * dv * hg * float((group_kept * rows).sum())
+        by = B * N * dqk * 2 + B * Hq * dqk * 2 + B * Hq * S * (dv + 1) * 4 + B * Hq * nk
+        out["%g" % lam] = dict(us=round(us, 2), GBs=round(by / us / 1e3, 1),
+                               frac_of_hbm_peak=round(by / us / 1e3 / HBM_PEAK_GBS, 4),
+                               tflops_executed=round((s_flops + pv_flops) / us / 1e6, 1),
+                               block_sparsity=round(float(sk.mean()), 5),
+                               pv_skipped_fraction=round(1.0 - float(group_kept.mean()), 5))
+    dense = out["0"]["us"]
+    for v in out.values():
+        v["speedup_vs_lambda0"] = round(dense / v["us"], 4)
+    by = B * N * dqk * 2
+    return dict(workload=w.name, B=B, Hq=Hq, d_qk=dqk, d_v=dv, context=N, Bc=Bc, num_splits=S,
+                heads_per_workgroup=hg, by_lambda=out,
+                hbm_roofline_us=round(by / (HBM_PEAK_GBS * 1e3), 2),
+                mfma_roofline_us_dense=round(2.0 * (dqk + dv) * N * Hq * B / (MFMA_BF16_PEAK_TFLOPS * 1e6), 2))
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo", encoding="utf-8") as fh:
@@ -403,6 +460,7 @@ def main():
 
     d = bench_decode(args, lib, torch, W)
     pre = None if args.no_prefill else bench_prefill(args, lib, torch, W)
+    mla = None if args.no_mla else bench_mla(args, lib, torch, W)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args, d)
 
     by = d["bytes"]
@@ -441,6 +499,7 @@ def main():
                    "block_sparsity": round(d["block_sparsity"], 5), "vload_sparsity": round(d["vload_sparsity"], 5),
                    "bytes": by},
         "prefill": pre,
+        "mla_decode": mla,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

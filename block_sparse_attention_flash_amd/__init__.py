@@ -20,8 +20,9 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["blasst_prefill", "blasst_decode", "blasst_decode_combine", "blasst_prefill_margins",
-           "blasst_decode_margins", "blasst_prefill_ragged", "blasst_decode_ragged", "status_string", "prefill",
-           "decode", "decode_combine", "prefill_margins", "decode_margins", "prefill_ragged", "decode_ragged",
+           "blasst_decode_margins", "blasst_prefill_ragged", "blasst_decode_ragged", "blasst_decode_mla", "status_string",
+           "prefill", "decode", "decode_combine", "prefill_margins", "decode_margins", "prefill_ragged",
+           "decode_ragged", "decode_mla",
            "BlasstError", "library_path", "build"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -69,6 +70,8 @@ def _load():
         lib.blasst_prefill_ragged.restype = i
         lib.blasst_decode_ragged.argtypes = [P, P, P, P, P, P, P, P, i, i, i, i, i, i, d, i, P]
         lib.blasst_decode_ragged.restype = i
+        lib.blasst_decode_mla.argtypes = [P, P, P, P, P, i, i, i, i, i, i, d, d, i, P]
+        lib.blasst_decode_mla.restype = i
         lib.blasst_status_string.argtypes = [i]
         lib.blasst_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -322,6 +325,43 @@ def decode_ragged(q, k, v, seq_lens, lam: float, num_splits: int, Bc: int = 128,
     vskip = torch.empty((B, Hkv, nk), dtype=torch.uint8, device=q.device) if with_masks else None
     blasst_decode_ragged(q, k, v, o_part, lse_part, skip, vskip, seq_lens, Bc, lam, num_splits)
     return o_part, lse_part, skip, vskip
+
+
+def blasst_decode_mla(q: torch.Tensor, kv: torch.Tensor, o_part: torch.Tensor, lse_part: torch.Tensor,
+                      skip_mask: Optional[torch.Tensor], Bc: int, softmax_scale: float, lam: float,
+                      num_splits: int, d_v: int = 512, stream=None) -> None:
+    """q [B,Hq,d_qk] (or [B,Hq,1,d_qk]), kv [B,N,d_qk] bf16; o_part [B,Hq,S,d_v], lse_part [B,Hq,S] fp32;
+    skip_mask [B,Hq,nk] uint8 or None."""
+    _need(q, "q", torch.bfloat16)
+    _need(kv, "kv", torch.bfloat16)
+    _need(o_part, "o_part", torch.float32)
+    _need(lse_part, "lse_part", torch.float32)
+    B, Hq, d_qk = q.shape[0], q.shape[1], q.shape[-1]
+    N = kv.shape[1]
+    S = num_splits
+    if q.numel() != B * Hq * d_qk or kv.shape != (B, N, d_qk):
+        raise ValueError("q must be [B,Hq,d_qk] and kv [B,N,d_qk]")
+    if o_part.shape != (B, Hq, S, d_v) or lse_part.shape != (B, Hq, S):
+        raise ValueError("o_part must be [B,Hq,S,d_v] and lse_part [B,Hq,S]")
+    if skip_mask is not None:
+        _need(skip_mask, "skip_mask", torch.uint8)
+        if skip_mask.shape != (B, Hq, -(-N // Bc)):
+            raise ValueError("skip_mask must be [B,Hq,nk]")
+    st = _load().blasst_decode_mla(_ptr(q), _ptr(kv), _ptr(o_part), _ptr(lse_part), _ptr(skip_mask), B, Hq, N,
+                                   d_qk, d_v, Bc, float(softmax_scale), float(lam), S, _stream(stream))
+    _check("blasst_decode_mla", st)
+
+
+def decode_mla(q, kv, lam: float, num_splits: int, softmax_scale: float, Bc: int = 64, d_v: int = 512,
+               with_mask: bool = True):
+    """Allocating wrapper: returns (o_part [B,Hq,S,d_v], lse_part [B,Hq,S], skip [B,Hq,nk] or None)."""
+    B, Hq = q.shape[0], q.shape[1]
+    N = kv.shape[1]
+    o_part = torch.empty((B, Hq, num_splits, d_v), dtype=torch.float32, device=q.device)
+    lse_part = torch.empty((B, Hq, num_splits), dtype=torch.float32, device=q.device)
+    skip = torch.empty((B, Hq, -(-N // Bc)), dtype=torch.uint8, device=q.device) if with_mask else None
+    blasst_decode_mla(q, kv, o_part, lse_part, skip, Bc, softmax_scale, lam, num_splits, d_v)
+    return o_part, lse_part, skip
 
 
 def decode_combine(o_part, lse_part):

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libblasst.so")
-SOURCES = ["api.cpp", "decode.hip", "prefill.hip"]
+SOURCES = ["api.cpp", "decode.hip", "prefill.hip", "mla.hip"]
 ARCH = os.environ.get("BLASST_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")

@@ -150,7 +150,7 @@ BLASST_EXPORT blasst_status blasst_decode_combine(const float* o_part, const flo
                                                   int B, int Hq, int d, int num_splits, blasst_stream_t stream) {
     try {
         if (B < 0 || Hq < 0 || d <= 0 || num_splits < 1) return BLASST_ERR_INVALID_ARG;
-        if (!supported_dim(d)) return BLASST_ERR_UNSUPPORTED;
+        if (!supported_dim(d) && d != 512) return BLASST_ERR_UNSUPPORTED;
         const int64_t rows = (int64_t)B * Hq;
         if (rows == 0) return BLASST_OK;  // nothing to do; pointers are not read
         if (!o_part || !lse_part || !o) return BLASST_ERR_INVALID_ARG;
@@ -247,4 +247,39 @@ BLASST_EXPORT const char* blasst_status_string(blasst_status status) {
         case BLASST_ERR_INTERNAL: return "internal error";
     }
     return "unknown status";
+}
+
+BLASST_EXPORT blasst_status blasst_decode_mla(const void* q, const void* kv, float* o_part, float* lse_part,
+                                              uint8_t* skip_mask, int B, int Hq, int N, int d_qk, int d_v, int Bc,
+                                              double softmax_scale, double lambda, int num_splits,
+                                              blasst_stream_t stream) {
+    try {
+        if (B < 0 || Hq < 0 || N <= 0 || d_qk <= 0 || d_v <= 0 || d_v > d_qk || Bc <= 0) return BLASST_ERR_INVALID_ARG;
+        if (!lambda_ok(lambda) || !(softmax_scale > 0.0) || !std::isfinite(softmax_scale))
+            return BLASST_ERR_INVALID_ARG;
+        const int64_t nk = ((int64_t)N + Bc - 1) / Bc;
+        if (num_splits < 1 || num_splits > nk) return BLASST_ERR_INVALID_ARG;
+        if (d_qk != 576 || d_v != 512 || Bc != 64 || Hq % 32 != 0) return BLASST_ERR_UNSUPPORTED;
+        if ((int64_t)B * Hq == 0) return BLASST_OK;  // nothing to do; pointers are not read
+        if (!q || !kv || !o_part || !lse_part) return BLASST_ERR_INVALID_ARG;
+        if (!aligned16(q) || !aligned16(kv) || !aligned16(o_part)) return BLASST_ERR_INVALID_ARG;
+        if (B > 65535 || (int64_t)N * 576 * B > ((int64_t)1 << 40)) return BLASST_ERR_UNSUPPORTED;
+
+        blasst::MlaArgs a;
+        a.q = static_cast<const uint16_t*>(q);
+        a.kv = static_cast<const uint16_t*>(kv);
+        a.o_part = o_part;
+        a.lse_part = lse_part;
+        a.skip = skip_mask;
+        a.B = B;
+        a.Hq = Hq;
+        a.N = N;
+        a.nk = (int)nk;
+        a.S = num_splits;
+        a.score_scale = static_cast<float>(softmax_scale * kLog2e);
+        a.thr = log2_threshold(lambda);
+        return from_hip(blasst::launch_decode_mla(a, reinterpret_cast<hipStream_t>(stream)));
+    } catch (...) {
+        return BLASST_ERR_INTERNAL;
+    }
 }

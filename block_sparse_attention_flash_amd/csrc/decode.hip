@@ -479,7 +479,9 @@ hipError_t launch_decode_margins(const DecodeArgs& a, int d, int Bc, hipStream_t
 
 hipError_t launch_decode_combine(const float* o_part, const float* lse_part, float* o, float* lse, int rows,
                                  int d, int S, hipStream_t stream) {
-    if (d == 128)
+    if (d == 512)
+        hipLaunchKernelGGL(decode_combine_kernel<512>, dim3(rows), dim3(512), 0, stream, o_part, lse_part, o, lse, S);
+    else if (d == 128)
         hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(rows), dim3(128), 0, stream, o_part, lse_part, o, lse, S);
     else
         hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(rows), dim3(64), 0, stream, o_part, lse_part, o, lse, S);

@@ -38,7 +38,20 @@ struct PrefillArgs {
     const int* lens = nullptr;  // ragged batch: [B] sequence lengths (device), clamped to [0, T]; T, nq = capacity
 };
 
+// MLA decode (absorbed latent form): 576-wide cache rows, value = the first 512 columns, Bc = 64.
+struct MlaArgs {
+    const uint16_t* q;   // bf16 [B, Hq, 576]
+    const uint16_t* kv;  // bf16 [B, N, 576]
+    float* o_part;       // [B, Hq, S, 512]
+    float* lse_part;     // [B, Hq, S]
+    uint8_t* skip;       // [B, Hq, nk] or null
+    int B, Hq, N, nk, S;
+    float score_scale;   // softmax scale * log2(e)
+    float thr;           // ln(lambda) * log2(e); -inf when lambda == 0
+};
+
 hipError_t launch_decode(const DecodeArgs& a, int d, int Bc, hipStream_t stream);
+hipError_t launch_decode_mla(const MlaArgs& a, hipStream_t stream);
 hipError_t launch_decode_combine(const float* o_part, const float* lse_part, float* o, float* lse, int rows,
                                  int d, int S, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, int d, int Bc, hipStream_t stream);

@@ -1,0 +1,272 @@
+// Split-KV MLA decode with the skip-softmax rule.
+//
+// Multi-head latent attention in its absorbed decode form: every query head
+// of a sequence reads the same cache row per token, 576 bf16 = a 512-wide
+// latent part followed by a 64-wide rotary part, and the value of a token is
+// its latent part.  BLASST blog, section on the decode kernel: with the KV
+// state compressed into the latent space, MLA decode can be compute bound, so
+// besides the V load (here V is part of the K row and is read anyway) a skip
+// must also save the softmax work -- the exp, the row sum and the P V product.
+// A head skips a block when its block max trails the running max by more than
+// ln(lambda) (Eq. 5); the P V step of a block runs only if some head of the
+// workgroup keeps it, and a skipping head's P is zero.
+//
+// One workgroup = 8 waves per (split, group of 16*NT heads, sequence); blocks
+// of 64 tokens.  Per block:
+//   copy     the block's 64 cache rows go HBM -> LDS (global_load_lds_dwordx4,
+//            whole rows per instruction), double-buffered: block j+1 is in
+//            flight while block j is computed.  Latent rows (1 KiB) are
+//            XOR-swizzled by 16-byte chunk within groups of 16 chunks, rotary
+//            rows (128 B) within their 8 chunks.
+//   S^T      K Q^T on MFMA 16x16x32 bf16 (16 keys x 16 heads per tile, 18
+//            k-steps over the 576 columns); wave w owns head tile w / (8/NT)
+//            and 16-key tiles, q^T stays in registers.  Block max per head
+//            through LDS, then every lane takes the decisions of its heads
+//            (prefix max: no cascade inside a block).
+//   P        2^(t - m) for kept heads, 0 otherwise, rounded to bf16 and stored
+//            head-major in LDS; each S wave keeps its heads' row-sum partials.
+//   O^T      += V^T P^T: wave w owns latent columns [64w, 64w + 64) of every
+//            head of the group, V^T read from the latent tile with
+//            ds_read_b64_tr_b16, P^T from LDS.  No cross-wave reduction of O.
+// Scores are in log2 units (t = s * scale * log2 e); the test reads
+// t~ - m < ln(lambda) * log2 e.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace blasst {
+
+namespace {
+
+constexpr int MLA_BC = 64;
+constexpr int MLA_DN = 512;  // latent columns (the value)
+constexpr int MLA_DR = 64;   // rotary columns
+constexpr int MLA_DQK = MLA_DN + MLA_DR;
+
+// physical 16-byte chunk of logical chunk c in latent row r (XOR within groups of 16)
+__device__ __forceinline__ int nope_chunk(int c, int r) { return (c & ~15) | ((c & 15) ^ (r & 15)); }
+
+template <int NT>
+__global__ __launch_bounds__(512) void mla_split_kernel(MlaArgs a) {
+    constexpr int W = 8;
+    constexpr int WPH = W / NT;                  // S waves per head tile
+    constexpr int KPW = 4 / WPH;                 // 16-key tiles per S wave
+    constexpr int HG = 16 * NT;                  // heads per workgroup
+    constexpr int NOPE_ROW = 2 * MLA_DN;         // 1024 B
+    constexpr int ROPE_ROW = 2 * MLA_DR;         // 128 B
+    constexpr int NOPE_TILE = MLA_BC * NOPE_ROW;
+    constexpr int STAGE = NOPE_TILE + MLA_BC * ROPE_ROW;
+    constexpr int PROW = 2 * MLA_BC + 16;        // one head's P^T row: 64 bf16 + 16 B pad
+    constexpr int KSTEPS = MLA_DQK / 32;         // 18
+    static_assert(NT == 2 || NT == 4, "16*NT heads per workgroup, NT in {2, 4}");
+
+    __shared__ __attribute__((aligned(16))) char lds_kv[2][STAGE];
+    __shared__ __attribute__((aligned(16))) char lds_p[HG * PROW];
+    __shared__ float lds_pmax[WPH][HG];
+    __shared__ float lds_l[WPH][HG];
+
+    const int split = blockIdx.x, hgrp = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, n = lane & 15;
+    const int N = a.N, nk = a.nk;
+    const int j0 = (int)((int64_t)split * nk / a.S);
+    const int j1 = (int)((int64_t)(split + 1) * nk / a.S);
+    const int h0 = hgrp * HG;
+    const uint16_t* kvb = a.kv + (size_t)b * N * MLA_DQK;
+
+    // S role: head tile sht, key tiles kt0 .. kt0 + KPW - 1
+    const int sht = wave / WPH, kt0 = (wave % WPH) * KPW;
+    bf16x8 qf[KSTEPS];
+    {
+        const uint16_t* qrow = a.q + ((size_t)b * a.Hq + h0 + 16 * sht + n) * MLA_DQK;
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) qf[s] = as_bf16x8(load16(qrow + 32 * s + 8 * g));
+    }
+
+    f32x4 oacc[NT][4];
+    float m_run[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        m_run[nt] = kNegInf;
+#pragma unroll
+        for (int dd = 0; dd < 4; ++dd) oacc[nt][dd] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    float l_part = 0.f;  // S role: row-sum partial of head 16*sht + n over this lane's keys
+
+    // Wave w copies rows 8w .. 8w + 7 of a block: one 1 KiB instruction per
+    // latent row (lane l lands at physical chunk l) and one for the 8 rotary
+    // rows (lane l -> row 8w + l/8, physical chunk l % 8).  Rows past the
+    // context re-read its last row.
+    auto issue = [&](int j, int stage) {
+        char* base = &lds_kv[stage][0];
+#pragma unroll
+        for (int r8 = 0; r8 < 8; ++r8) {
+            const int r = 8 * wave + r8;
+            const int key = min(j * MLA_BC + r, N - 1);
+            const int c = nope_chunk(lane, r);
+            global_to_lds16(kvb + (size_t)key * MLA_DQK + 8 * c, lds_addr(base + r * NOPE_ROW));
+        }
+        const int r = 8 * wave + (lane >> 3);
+        const int key = min(j * MLA_BC + r, N - 1);
+        const int c = (lane & 7) ^ (r & 7);
+        global_to_lds16(kvb + (size_t)key * MLA_DQK + MLA_DN + 8 * c, lds_addr(base + NOPE_TILE + 8 * wave * ROPE_ROW));
+    };
+
+    if (j0 < j1) issue(j0, 0);
+    for (int j = j0; j < j1; ++j) {
+        const int st = (j - j0) & 1;
+        // this block's rows have landed (every wave's copies) and the previous
+        // block's P and stage are no longer read
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (j + 1 < j1) issue(j + 1, st ^ 1);
+        const char* kvt = &lds_kv[st][0];
+
+        // ---- S^T tiles of this wave
+        f32x4 sacc[KPW];
+#pragma unroll
+        for (int kk = 0; kk < KPW; ++kk) sacc[kk] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) {
+#pragma unroll
+            for (int kk = 0; kk < KPW; ++kk) {
+                const int r = 16 * (kt0 + kk) + n;
+                const int c = 4 * (s < 16 ? s : s - 16) + g;
+                const int off = s < 16 ? r * NOPE_ROW + (nope_chunk(c, r) << 4)
+                                       : NOPE_TILE + r * ROPE_ROW + ((c ^ (r & 7)) << 4);
+                const u32x4 kf = *(const u32x4*)(kvt + off);
+                sacc[kk] = mfma16x16x32(as_bf16x8(kf), qf[s], sacc[kk]);
+            }
+        }
+        float pm = kNegInf;
+#pragma unroll
+        for (int kk = 0; kk < KPW; ++kk)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int key = j * MLA_BC + 16 * (kt0 + kk) + 4 * g + i;
+                float x = sacc[kk][i] * a.score_scale;
+                x = key < N ? x : kNegInf;
+                sacc[kk][i] = x;
+                pm = fmaxf(pm, x);
+            }
+        pm = wave_max_xor32(wave_max_xor16(pm));
+        if (g == 0) lds_pmax[wave % WPH][16 * sht + n] = pm;
+        __syncthreads();
+
+        // ---- decisions for head n of every head tile (Eq. 1, then Eq. 5)
+        bool keep[NT];
+        float alpha[NT];
+        bool any_keep = false;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            float bm = kNegInf;
+#pragma unroll
+            for (int w = 0; w < WPH; ++w) bm = fmaxf(bm, lds_pmax[w][16 * nt + n]);
+            const float m_new = fmaxf(m_run[nt], bm);
+            keep[nt] = !((bm - m_new) < a.thr);
+            alpha[nt] = exp2_fast(m_run[nt] - m_new);
+            m_run[nt] = m_new;
+            any_keep = any_keep || keep[nt];
+        }
+        if (a.skip != nullptr && wave == 0 && g == 0) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                a.skip[((size_t)b * a.Hq + h0 + 16 * nt + n) * nk + j] = (uint8_t)!keep[nt];
+        }
+        // the P V step runs iff some head of the group keeps the block
+        const bool vkeep = __builtin_amdgcn_readfirstlane((int)(__ballot(any_keep) != 0)) != 0;
+
+        // ---- P of this wave's tiles (0 for a skipping head), row-sum partials
+        {
+            bool kp = keep[0];
+            float mm = m_run[0], al = alpha[0];
+#pragma unroll
+            for (int nt = 1; nt < NT; ++nt)
+                if (sht == nt) { kp = keep[nt]; mm = m_run[nt]; al = alpha[nt]; }
+            l_part *= al;
+            if (vkeep) {
+#pragma unroll
+                for (int kk = 0; kk < KPW; ++kk) {
+                    float p[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float e = exp2_fast(sacc[kk][i] - mm);
+                        p[i] = kp ? e : 0.f;
+                    }
+                    l_part += (p[0] + p[1]) + (p[2] + p[3]);
+                    const u32x2 w2 = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+                    *(u32x2*)(lds_p + (16 * sht + n) * PROW + 2 * (16 * (kt0 + kk) + 4 * g)) = w2;
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---- O^T += V^T P^T for latent columns [64 wave, 64 wave + 64)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int dd = 0; dd < 4; ++dd) oacc[nt][dd] *= alpha[nt];
+        if (vkeep) {
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                // B = P^T: k-slots 0..3 = keys 32ks + 4g + i, 4..7 = keys 32ks + 16 + 4g + i
+                bf16x8 pf[NT];
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    const char* prow = lds_p + (16 * nt + n) * PROW + 2 * (32 * ks + 4 * g);
+                    const u32x2 lo = *(const u32x2*)prow;
+                    const u32x2 hi = *(const u32x2*)(prow + 32);
+                    pf[nt] = as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y});
+                }
+#pragma unroll
+                for (int dd = 0; dd < 4; ++dd) {
+                    const int dt = 4 * wave + dd;
+                    const int cc = 2 * dt + ((n & 3) >> 1);
+                    const int r0 = 32 * ks + 4 * g + (n >> 2), r1 = r0 + 16;
+                    const u32x2 lo = lds_read_tr16((const lds_char*)(kvt + r0 * NOPE_ROW + (nope_chunk(cc, r0) << 4) + (n & 1) * 8));
+                    const u32x2 hi = lds_read_tr16((const lds_char*)(kvt + r1 * NOPE_ROW + (nope_chunk(cc, r1) << 4) + (n & 1) * 8));
+                    const bf16x8 av = as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y});
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) oacc[nt][dd] = mfma16x16x32(av, pf[nt], oacc[nt][dd]);
+                }
+            }
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+    // ---- epilogue: l per head from the S waves' partials, O / l and LSE
+    {
+        const float lw = wave_sum_xor32(wave_sum_xor16(l_part));
+        if (g == 0) lds_l[wave % WPH][16 * sht + n] = lw;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        float l = 0.f;
+#pragma unroll
+        for (int w = 0; w < WPH; ++w) l += lds_l[w][16 * nt + n];
+        const float inv = l > 0.f ? 1.f / l : 0.f;  // 0: a split with no block
+        const size_t orow = ((size_t)b * a.Hq + h0 + 16 * nt + n) * a.S + split;
+#pragma unroll
+        for (int dd = 0; dd < 4; ++dd) {
+            const f32x4 o = oacc[nt][dd] * inv;
+            *(f32x4*)(a.o_part + orow * MLA_DN + 16 * (4 * wave + dd) + 4 * g) = o;
+        }
+        if (wave == 0 && g == 0) a.lse_part[orow] = l > 0.f ? m_run[nt] * kLn2 + logf(l) : kNegInf;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_decode_mla(const MlaArgs& a, hipStream_t stream) {
+    // 64 heads per workgroup when that still gives every CU a workgroup, else 32
+    const bool wide = a.Hq % 64 == 0 && (int64_t)a.S * (a.Hq / 64) * a.B >= 256;
+    if (wide) {
+        hipLaunchKernelGGL(mla_split_kernel<4>, dim3(a.S, a.Hq / 64, a.B), dim3(512), 0, stream, a);
+    } else {
+        hipLaunchKernelGGL(mla_split_kernel<2>, dim3(a.S, a.Hq / 32, a.B), dim3(512), 0, stream, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace blasst

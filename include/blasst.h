@@ -147,6 +147,38 @@ blasst_status blasst_decode_ragged(const void* q, const void* k, const void* v, 
                                    blasst_stream_t stream);
 
 /*
+ * MLA decode: multi-head latent attention in its absorbed decode form (the
+ * variant named in the BLASST blog's section on the decode kernel: MLA decode
+ * can be compute bound, so a skip also saves the softmax -- the exp, the row
+ * sum and the P V product -- not only a V load).  Every query head of sequence
+ * b reads the same cache row per token, [latent (d_v) | rotary (d_qk - d_v)];
+ * the value of token t is its latent part kv[b, t, 0 .. d_v).  Scores are
+ * (q . kv_t) * softmax_scale.  Blocks of Bc tokens, num_splits contiguous
+ * splits each restarting the running max, and per-head decisions exactly as in
+ * blasst_decode (each head decides alone); the P V product of a block is
+ * formed only for heads that keep it.  Merge the splits with
+ * blasst_decode_combine (d = d_v).
+ *
+ *   q          bf16 [B, Hq, d_qk]          (absorbed queries)
+ *   kv         bf16 [B, N, d_qk]           (latent cache rows)
+ *   o_part     fp32 [B, Hq, num_splits, d_v]
+ *   lse_part   fp32 [B, Hq, num_splits]    natural log
+ *   skip_mask  u8   [B, Hq, ceil(N/Bc)] or NULL   per-head decision
+ *   softmax_scale  the model's scale (e.g. 1/sqrt(192) for 128 + 64 query
+ *              columns before absorption); finite and > 0
+ *   num_splits 1 <= num_splits <= ceil(N/Bc)
+ * Built for d_qk = 576, d_v = 512, Bc = 64 and Hq a multiple of 32.
+ * Errors: INVALID_ARG for a null q/kv/o_part/lse_part, B/Hq < 0, N <= 0,
+ * d_v > d_qk, a bad scale or lambda, bad num_splits, a misaligned pointer;
+ * UNSUPPORTED for other d_qk/d_v/Bc or Hq not a multiple of 32.  Scalar
+ * arguments are checked first; then B*Hq == 0 returns OK and does nothing.
+ */
+blasst_status blasst_decode_mla(const void* q, const void* kv, float* o_part, float* lse_part,
+                                uint8_t* skip_mask, int B, int Hq, int N, int d_qk, int d_v, int Bc,
+                                double softmax_scale, double lambda, int num_splits,
+                                blasst_stream_t stream);
+
+/*
  * Merge of the splits by their true normalisers (SANTA notes, merge of
  * FlashDecoding tiles): LSE = ln sum_s exp(lse_s), O = sum_s exp(lse_s - LSE) O_s.
  * A split with lse_s = -inf contributes nothing; when every split has
@@ -157,7 +189,7 @@ blasst_status blasst_decode_ragged(const void* q, const void* k, const void* v, 
  *   o          fp32 [B, Hq, d]
  *   lse        fp32 [B, Hq] or NULL
  * Errors: INVALID_ARG for a null o_part/lse_part/o, B/Hq < 0, num_splits < 1,
- * d <= 0; UNSUPPORTED for d outside {64, 128}.  B*Hq == 0 returns OK without
+ * d <= 0; UNSUPPORTED for d outside {64, 128, 512} (512: MLA's latent width).  B*Hq == 0 returns OK without
  * reading the pointers.
  */
 blasst_status blasst_decode_combine(const float* o_part, const float* lse_part, float* o,

@@ -188,3 +188,44 @@ def check_prefill(x: dict, Bc: int, lam: float, causal=True, units=None, x_dev=N
         compare_rows(og, ref["o"][ui][: r1 - r0], rep, "o b=%d hq=%d i=%d" % (b, hq, i))
         compare_lse(lg, ref["lse"][ui][: r1 - r0], rep, "lse b=%d hq=%d i=%d" % (b, hq, i))
     return rep
+
+
+# --------------------------------------------------------------------------- #
+# MLA decode
+# --------------------------------------------------------------------------- #
+def run_gpu_mla(q_dev, kv_dev, Bc, lam, S, scale, dv):
+    import torch
+    import block_sparse_attention_flash_amd as bsa
+    o_part, lse_part, skip = bsa.decode_mla(q_dev, kv_dev, lam, S, scale, Bc=Bc, d_v=dv)
+    o, lse = bsa.decode_combine(o_part, lse_part)
+    torch.cuda.synchronize()
+    return {k: t.cpu().numpy() for k, t in dict(o_part=o_part, lse_part=lse_part, skip=skip, o=o, lse=lse).items()}
+
+
+def check_mla(q: np.ndarray, kv: np.ndarray, Bc: int, lam: float, S: int, scale: float, dv: int, units=None,
+              gpu=None) -> Report:
+    """Compare the GPU MLA decode (+ combine) with the oracle on (b, h) units b*Hq + h."""
+    B, Hq = q.shape[0], q.shape[1]
+    if gpu is None:
+        gpu = run_gpu_mla(to_device(q), to_device(kv), Bc, lam, S, scale, dv)
+    units = list(range(B * Hq)) if units is None else list(units)
+    ref = oracle.decode_mla(q, kv, Bc, lam, S, scale, dv, units=units)
+    rep = Report()
+    force = np.full(ref["skip"].shape, -1, np.int8)
+    any_flip = False
+    for ui, u in enumerate(units):
+        b, h = divmod(u, Hq)
+        diff = compare_masks(gpu["skip"][b, h], ref["skip"][ui], ref["margin"][ui], rep, "skip b=%d h=%d" % (b, h))
+        if diff.any():
+            any_flip = True
+            force[ui][diff] = gpu["skip"][b, h][diff]
+    if any_flip:
+        ref = oracle.decode_mla(q, kv, Bc, lam, S, scale, dv, units=units, force=force)
+    o_ref, lse_ref = oracle.combine(ref["o_part"], ref["lse_part"])
+    for ui, u in enumerate(units):
+        b, h = divmod(u, Hq)
+        compare_rows(gpu["o_part"][b, h], ref["o_part"][ui], rep, "o_part b=%d h=%d" % (b, h))
+        compare_lse(gpu["lse_part"][b, h], ref["lse_part"][ui], rep, "lse_part b=%d h=%d" % (b, h))
+        compare_rows(gpu["o"][b, h][None], o_ref[ui][None], rep, "o b=%d h=%d" % (b, h))
+        compare_lse(gpu["lse"][b, h][None], lse_ref[ui][None], rep, "lse b=%d h=%d" % (b, h))
+    return rep

@@ -27,8 +27,9 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert declared() == ["blasst_decode", "blasst_decode_combine", "blasst_decode_margins", "blasst_decode_ragged",
-                          "blasst_prefill", "blasst_prefill_margins", "blasst_prefill_ragged", "blasst_status_string"]
+    assert declared() == ["blasst_decode", "blasst_decode_combine", "blasst_decode_margins", "blasst_decode_mla",
+                          "blasst_decode_ragged", "blasst_prefill", "blasst_prefill_margins", "blasst_prefill_ragged",
+                          "blasst_status_string"]
 
 
 def test_exports_match_header(lib):
@@ -147,3 +148,26 @@ def test_prefill_ragged_validation(lib, kw, status):
 ])
 def test_decode_ragged_validation(lib, kw, status):
     assert decode_ragged(lib, **kw) == status
+
+
+def decode_mla(lib, q=FAKE, kv=FAKE, B=2, Hq=128, N=4096, dqk=576, dv=512, Bc=64, scale=0.0722, lam=1e-3, S=4):
+    f = lib.blasst_decode_mla
+    f.argtypes = [P, P, P, P, P, I, I, I, I, I, I, D, D, I, P]
+    return f(q, kv, FAKE, FAKE, None, B, Hq, N, dqk, dv, Bc, scale, lam, S, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(kv=None), 1), (dict(kv=P(0x1004)), 1), (dict(N=0), 1), (dict(S=0), 1),
+    (dict(S=65), 1), (dict(dv=600), 1), (dict(scale=0.0), 1), (dict(scale=float("inf")), 1),
+    (dict(scale=float("nan")), 1), (dict(lam=1.0), 1), (dict(dqk=128, dv=128), 2), (dict(Bc=128), 2),
+    (dict(Hq=16), 2), (dict(Hq=48), 2), (dict(B=0), 0), (dict(Hq=0), 0),
+])
+def test_decode_mla_validation(lib, kw, status):
+    assert decode_mla(lib, **kw) == status
+
+
+def test_combine_accepts_the_latent_width(lib):
+    f = lib.blasst_decode_combine
+    f.argtypes = [P, P, P, P, I, I, I, I, P]
+    assert f(FAKE, FAKE, FAKE, None, 0, 128, 512, 16, None) == 0   # B = 0: validated, nothing launched
+    assert f(FAKE, FAKE, FAKE, None, 0, 128, 256, 16, None) == 2
