@@ -77,7 +77,7 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--copies", type=int, default=4, help="KV copies rotated to defeat the Infinity Cache")
-    p.add_argument("--prefill-reps", type=int, default=5)
+    p.add_argument("--prefill-reps", type=int, default=5, help="launches per prefill timing trial")
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-mla", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -287,13 +287,27 @@ def bench_decode(args, lib, torch, W):
     torch.cuda.synchronize()
     dense_step_ms = start.elapsed_time(stop) / args.steps
 
+    # the dense reference: no block ever skipped and no decision bytes (blasst_decode_dense)
+    ref_args = [(P(c["q"]), P(c["k"]), P(c["v"]), P(o_part), P(lse_part), B, Hq, N, d, w.G, Bc, S, sp) for c in copies]
+    for s in range(args.warmup):
+        check(lib.blasst_decode_dense(*ref_args[s % len(ref_args)]))
+    torch.cuda.synchronize()
+    start.record(stream)
+    for s in range(args.steps):
+        check(lib.blasst_decode_dense(*ref_args[s % len(ref_args)]))
+        check(combine_fn(*comb))
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ref_step_ms = start.elapsed_time(stop) / args.steps
+
     # decisions of the timed configuration (identical on every copy)
     check(decode_fn(*sargs[0]))
     torch.cuda.synchronize()
     sk, vsk = skip.cpu().numpy(), vskip.cpu().numpy()
     by = decode_bytes(w, vsk)
     return dict(w=w, x=x, step_ms=step_ms, split_ms=split_ms, split_trials_ms=trials, dense_step_ms=dense_step_ms,
-                wall=wall, bytes=by, block_sparsity=float(sk.mean()), vload_sparsity=float(vsk.mean()))
+                ref_step_ms=ref_step_ms, wall=wall, bytes=by, block_sparsity=float(sk.mean()),
+                vload_sparsity=float(vsk.mean()))
 
 
 def bench_prefill(args, lib, torch, W):
@@ -309,32 +323,47 @@ def bench_prefill(args, lib, torch, W):
     out = {}
     visited = B * Hq * nq * (nq + 1) // 2
     tile_flops = 2.0 * Bc * Bc * d
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def timed(fn, a):
+        """TRIALS trials of prefill_reps back-to-back launches (after 2 warm-ups); median, min, max in ms."""
+        for _ in range(2):
+            assert fn(*a) == 0
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(TRIALS):
+            s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s0.record(stream)
+            for _ in range(args.prefill_reps):
+                assert fn(*a) == 0
+            s1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(s0.elapsed_time(s1) / args.prefill_reps)
+        return float(np.median(ts)), min(ts), max(ts)
+
     for lam in (0.0,) + tuple(w.lambdas):
         a = (P(x["q"]), P(x["k"]), P(x["v"]), P(o), P(lse), P(mask), B, Hq, T, d, w.G, Bc,
-             ctypes.c_double(lam), 1, ctypes.c_void_p(stream.cuda_stream))
-        for _ in range(2):
-            assert lib.blasst_prefill(*a) == 0
-        torch.cuda.synchronize()
-        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s0.record(stream)
-        for _ in range(args.prefill_reps):
-            assert lib.blasst_prefill(*a) == 0
-        s1.record(stream)
-        torch.cuda.synchronize()
-        ms = s0.elapsed_time(s1) / args.prefill_reps
+             ctypes.c_double(lam), 1, sp)
+        ms, ms_min, ms_max = timed(lib.blasst_prefill, a)
         m = mask.cpu().numpy()
         skipped = int((m == 1).sum())
         kept = visited - skipped
         flops = (visited + kept) * tile_flops
         tflops = flops / (ms * 1e-3) / 1e12
-        out["%g" % lam] = dict(ms=round(ms, 4), tflops_executed=round(tflops, 2),
+        out["%g" % lam] = dict(ms=round(ms, 4), ms_min=round(ms_min, 4), ms_max=round(ms_max, 4),
+                               tflops_executed=round(tflops, 2),
                                frac_of_mfma_peak=round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                                block_sparsity=round(skipped / visited, 5),
                                executed_tflop=round(flops / 1e12, 4))
     dense = out["0"]["ms"]
     for k, v in out.items():
         v["speedup_vs_lambda0"] = round(dense / v["ms"], 4)
-    return dict(workload=w.name, B=B, Hq=Hq, Hkv=w.Hkv, d=d, T=T, Bc=Bc, by_lambda=out,
+    # the kernel built without the skip test (blasst_prefill_dense): what the test costs at 0% sparsity
+    ref_ms, _, _ = timed(lib.blasst_prefill_dense,
+                         (P(x["q"]), P(x["k"]), P(x["v"]), P(o), P(lse), B, Hq, T, d, w.G, Bc, 1, sp))
+    no_test = dict(ms=round(ref_ms, 4), tflops=round(2 * visited * tile_flops / (ref_ms * 1e-3) / 1e12, 2),
+                   lambda0_speed_vs_no_test=round(ref_ms / dense, 4))
+    return dict(workload=w.name, B=B, Hq=Hq, Hkv=w.Hkv, d=d, T=T, Bc=Bc, by_lambda=out, no_skip_test=no_test,
                 hbm_traffic_bytes_per_launch=measured_traffic("prefill_kernel", w.name))
 
 
@@ -496,6 +525,8 @@ def main():
                                               "max": round(max(d["split_trials_ms"]) * 1e3, 3)},
                    "dense_step_us": round(d["dense_step_ms"] * 1e3, 3),
                    "speedup_vs_lambda0": round(d["dense_step_ms"] / d["step_ms"], 4),
+                   "no_skip_step_us": round(d["ref_step_ms"] * 1e3, 3),
+                   "lambda0_speed_vs_no_skip": round(d["ref_step_ms"] / d["dense_step_ms"], 4),
                    "block_sparsity": round(d["block_sparsity"], 5), "vload_sparsity": round(d["vload_sparsity"], 5),
                    "bytes": by},
         "prefill": pre,

@@ -20,7 +20,8 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["blasst_prefill", "blasst_decode", "blasst_decode_combine", "blasst_prefill_margins",
-           "blasst_decode_margins", "blasst_prefill_ragged", "blasst_decode_ragged", "blasst_decode_mla", "status_string",
+           "blasst_decode_margins", "blasst_prefill_ragged", "blasst_decode_ragged", "blasst_decode_mla", "blasst_prefill_dense",
+           "blasst_decode_dense", "status_string",
            "prefill", "decode", "decode_combine", "prefill_margins", "decode_margins", "prefill_ragged",
            "decode_ragged", "decode_mla",
            "BlasstError", "library_path", "build"]
@@ -72,6 +73,10 @@ def _load():
         lib.blasst_decode_ragged.restype = i
         lib.blasst_decode_mla.argtypes = [P, P, P, P, P, i, i, i, i, i, i, d, d, i, P]
         lib.blasst_decode_mla.restype = i
+        lib.blasst_prefill_dense.argtypes = [P, P, P, P, P, i, i, i, i, i, i, i, P]
+        lib.blasst_prefill_dense.restype = i
+        lib.blasst_decode_dense.argtypes = [P, P, P, P, P, i, i, i, i, i, i, i, P]
+        lib.blasst_decode_dense.restype = i
         lib.blasst_status_string.argtypes = [i]
         lib.blasst_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -185,6 +190,24 @@ def blasst_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o_part: tor
                                _ptr(vskip_mask), B, Hq, N, d, Hq // Hkv, Bc, float(lam), int(bool(causal)),
                                num_splits, _stream(stream))
     _check("blasst_decode", st)
+
+
+def blasst_prefill_dense(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                         lse: Optional[torch.Tensor], Bc: int, causal: bool = True, stream=None) -> None:
+    """blasst_prefill without the skip test (every tile kept)."""
+    B, Hq, T, d, Hkv = _prefill_shapes(q, k, v, o, lse, None, Bc)
+    st = _load().blasst_prefill_dense(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, T, d, Hq // Hkv, Bc,
+                                      int(bool(causal)), _stream(stream))
+    _check("blasst_prefill_dense", st)
+
+
+def blasst_decode_dense(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o_part: torch.Tensor,
+                        lse_part: torch.Tensor, Bc: int, num_splits: int, stream=None) -> None:
+    """blasst_decode without the skip test (every block kept, V always loaded)."""
+    B, Hq, N, d, Hkv = _decode_shapes(q, k, v, o_part, lse_part, None, None, Bc, num_splits)
+    st = _load().blasst_decode_dense(_ptr(q), _ptr(k), _ptr(v), _ptr(o_part), _ptr(lse_part), B, Hq, N, d,
+                                     Hq // Hkv, Bc, num_splits, _stream(stream))
+    _check("blasst_decode_dense", st)
 
 
 def blasst_decode_ragged(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o_part: torch.Tensor,

@@ -34,7 +34,7 @@ namespace {
 
 blasst_status prefill_impl(const void* q, const void* k, const void* v, float* o, float* lse, uint8_t* skip_mask,
                            const int32_t* seq_lens, int B, int Hq, int T, int d, int gqa_ratio, int Bc,
-                           double lambda, int causal, blasst_stream_t stream) {
+                           double lambda, int causal, blasst_stream_t stream, bool dense = false) {
     try {
         if (B < 0 || Hq < 0 || T < 0 || d <= 0 || Bc <= 0 || gqa_ratio < 1) return BLASST_ERR_INVALID_ARG;
         if (Hq % gqa_ratio != 0 || !lambda_ok(lambda) || (causal != 0 && causal != 1))
@@ -64,6 +64,7 @@ blasst_status prefill_impl(const void* q, const void* k, const void* v, float* o
         a.score_scale = static_cast<float>(kLog2e / std::sqrt((double)d));
         a.thr = log2_threshold(lambda);
         a.lens = seq_lens;
+        a.dense = dense;
         return from_hip(blasst::launch_prefill(a, d, Bc, reinterpret_cast<hipStream_t>(stream)));
     } catch (...) {
         return BLASST_ERR_INTERNAL;
@@ -127,6 +128,22 @@ BLASST_EXPORT blasst_status blasst_prefill_ragged(const void* q, const void* k, 
                                                   blasst_stream_t stream) {
     if ((int64_t)B * Hq * T != 0 && !lens_ok(seq_lens)) return BLASST_ERR_INVALID_ARG;
     return prefill_impl(q, k, v, o, lse, skip_mask, seq_lens, B, Hq, T, d, gqa_ratio, Bc, lambda, causal, stream);
+}
+
+BLASST_EXPORT blasst_status blasst_prefill_dense(const void* q, const void* k, const void* v, float* o, float* lse,
+                                                 int B, int Hq, int T, int d, int gqa_ratio, int Bc, int causal,
+                                                 blasst_stream_t stream) {
+    return prefill_impl(q, k, v, o, lse, nullptr, nullptr, B, Hq, T, d, gqa_ratio, Bc, 0.0, causal, stream, true);
+}
+
+BLASST_EXPORT blasst_status blasst_decode_dense(const void* q, const void* k, const void* v, float* o_part,
+                                                float* lse_part, int B, int Hq, int N, int d, int gqa_ratio, int Bc,
+                                                int num_splits, blasst_stream_t stream) {
+    // The decode test is one compare per (head, block) inside a batched decision; building
+    // it out changes only register allocation, so the reference runs the same kernel with
+    // the threshold at -inf (the compare never fires) and writes no decision bytes.
+    return decode_impl(q, k, v, o_part, lse_part, nullptr, nullptr, nullptr, B, Hq, N, d, gqa_ratio, Bc, 0.0, 1,
+                       num_splits, stream);
 }
 
 BLASST_EXPORT blasst_status blasst_decode(const void* q, const void* k, const void* v, float* o_part,

@@ -36,6 +36,7 @@ struct PrefillArgs {
     float thr;
     float* margin = nullptr;  // margin pass only: [B, Hq, nq, nk]
     const int* lens = nullptr;  // ragged batch: [B] sequence lengths (device), clamped to [0, T]; T, nq = capacity
+    bool dense = false;         // the kernel built without the skip test (every tile kept)
 };
 
 // MLA decode (absorbed latent form): 576-wide cache rows, value = the first 512 columns, Bc = 64.

@@ -46,7 +46,9 @@ constexpr int PRIO_Y = BLASST_PREFILL_PRIO_Y;
 #endif
 constexpr int PFV = BLASST_PREFILL_PFV;  // V^T prefetch distance in 16-key sub-tiles
 
-template <int D, int BC, int HPW>
+// SKIP = false builds the same kernel without the skip test (every tile kept,
+// no vote): the dense reference the test's cost is measured against.
+template <int D, int BC, int HPW, bool SKIP = true>
 __global__ __launch_bounds__(2 * BC * HPW) void prefill_kernel(PrefillArgs a) {
     constexpr int NWH = BC / 32;           // waves per head
     constexpr int NW = NWH * HPW;          // waves per workgroup
@@ -220,16 +222,20 @@ __global__ __launch_bounds__(2 * BC * HPW) void prefill_kernel(PrefillArgs a) {
         mt = wave_max_xor32(mt);
         // Eq. 1 then the log-space test (log2 units)
         m_new = fmaxf(m, mt);
-        const bool vote_skip = !row_ok || mt == kNegInf || (mt - m_new) * c < a.thr;
-        const bool wave_skip = __all(vote_skip);
-        if (lane == 0) lds_vote[wave] = wave_skip;
+        if constexpr (SKIP) {
+            const bool vote_skip = !row_ok || mt == kNegInf || (mt - m_new) * c < a.thr;
+            const bool wave_skip = __all(vote_skip);
+            if (lane == 0) lds_vote[wave] = wave_skip;
+        }
     };
 
     // ---- phase Y_j: AND over the head's waves; kept tile -> rescale, P, row sum, O^T += V^T P^T
     auto phase_y = [&](int j) {
-        bool skip = true;
+        bool skip = SKIP;
+        if constexpr (SKIP) {
 #pragma unroll
-        for (int w = 0; w < NWH; ++w) skip = skip && lds_vote[hsub * NWH + w];
+            for (int w = 0; w < NWH; ++w) skip = skip && lds_vote[hsub * NWH + w];
+        }
         if (wrow == 0 && lane == 0 && mask_row) mask_row[j] = (uint8_t)skip;
         if (skip) return;
         if (!__all(m_new == m)) {  // rescale only when some row's max moved
@@ -365,7 +371,10 @@ __global__ __launch_bounds__(2 * BC * HPW) void prefill_kernel(PrefillArgs a) {
 template <int D, int BC, int HPW>
 hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
     const dim3 grid((unsigned)a.nq * a.B * (a.Hq / HPW));
-    hipLaunchKernelGGL((prefill_kernel<D, BC, HPW>), grid, dim3(2 * BC * HPW), 0, stream, a);
+    if (a.dense)
+        hipLaunchKernelGGL((prefill_kernel<D, BC, HPW, false>), grid, dim3(2 * BC * HPW), 0, stream, a);
+    else
+        hipLaunchKernelGGL((prefill_kernel<D, BC, HPW, true>), grid, dim3(2 * BC * HPW), 0, stream, a);
     return hipGetLastError();
 }
 

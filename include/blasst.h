@@ -111,6 +111,24 @@ blasst_status blasst_decode(const void* q, const void* k, const void* v, float* 
                             int causal, int num_splits, blasst_stream_t stream);
 
 /*
+ * Dense references: blasst_prefill built without the skip test (no row votes,
+ * no vote exchange between waves, every tile kept), and blasst_decode with no
+ * block ever skipped (its test, one compare per head and block inside the
+ * batched decision, runs with the threshold at -inf) -- both without decision
+ * bytes.  Same arguments minus lambda and the masks; results equal the
+ * lambda = 0 calls.  They exist to measure what the test costs when nothing is
+ * skipped (the blog's 0.96-1.00x at 0% sparsity, section on the decision
+ * cost), and serve callers that want plain attention.
+ * Errors as blasst_prefill / blasst_decode.
+ */
+blasst_status blasst_prefill_dense(const void* q, const void* k, const void* v, float* o, float* lse,
+                                   int B, int Hq, int T, int d, int gqa_ratio, int Bc, int causal,
+                                   blasst_stream_t stream);
+blasst_status blasst_decode_dense(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
+                                  int B, int Hq, int N, int d, int gqa_ratio, int Bc, int num_splits,
+                                  blasst_stream_t stream);
+
+/*
  * Ragged batches: one length per sequence (the serving-shaped form of the same
  * two calls).  The tensors keep their padded layout -- T (prefill) or N
  * (decode) is the capacity, the row stride of every sequence -- and sequence b

@@ -27,9 +27,9 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert declared() == ["blasst_decode", "blasst_decode_combine", "blasst_decode_margins", "blasst_decode_mla",
-                          "blasst_decode_ragged", "blasst_prefill", "blasst_prefill_margins", "blasst_prefill_ragged",
-                          "blasst_status_string"]
+    assert declared() == ["blasst_decode", "blasst_decode_combine", "blasst_decode_dense", "blasst_decode_margins",
+                          "blasst_decode_mla", "blasst_decode_ragged", "blasst_prefill", "blasst_prefill_dense",
+                          "blasst_prefill_margins", "blasst_prefill_ragged", "blasst_status_string"]
 
 
 def test_exports_match_header(lib):
@@ -171,3 +171,16 @@ def test_combine_accepts_the_latent_width(lib):
     f.argtypes = [P, P, P, P, I, I, I, I, P]
     assert f(FAKE, FAKE, FAKE, None, 0, 128, 512, 16, None) == 0   # B = 0: validated, nothing launched
     assert f(FAKE, FAKE, FAKE, None, 0, 128, 256, 16, None) == 2
+
+
+def test_dense_references_validate_like_the_plain_calls(lib):
+    f = lib.blasst_prefill_dense
+    f.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, P]
+    assert f(None, FAKE, FAKE, FAKE, None, 1, 4, 256, 128, 4, 128, 1, None) == 1
+    assert f(FAKE, FAKE, FAKE, FAKE, None, 1, 4, 256, 96, 4, 128, 1, None) == 2
+    assert f(FAKE, FAKE, FAKE, FAKE, None, 0, 4, 256, 128, 4, 128, 1, None) == 0
+    g = lib.blasst_decode_dense
+    g.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, P]
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4, 256, 128, 4, 128, 3, None) == 1   # 3 splits > 2 blocks
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4, 256, 128, 4, 256, 1, None) == 2
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 4, 256, 128, 4, 128, 1, None) == 0
