@@ -53,7 +53,11 @@ __device__ __forceinline__ void wait_vm(int n) {
 // block) D = (m~ - m_new) in natural-log units and for every block the max of D
 // over the group's heads (skipped / V not loaded at lambda iff below ln lambda);
 // no V pass, no partial outputs.
-template <int D, int BC, int NT, int UW, int W, int NSLOT, bool MARGINS = false>
+// DSPLIT = 2: two workgroups per split, each forming the V pass for one half
+// of the d columns; both run the same K pass and decisions (the second one's
+// K reads hit the L2 the first one filled: the pair sits on one XCD), so each
+// CU streams K plus half of V instead of K plus all of V.
+template <int D, int BC, int NT, int UW, int W, int NSLOT, bool MARGINS = false, int DSPLIT = 1>
 __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
     constexpr int KG = BC / 32;           // 32-key units per block
     constexpr int UPP = W * UW;           // units per phase
@@ -63,17 +67,33 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
     constexpr int FR = D / 16;            // 16-byte fragments per lane per unit
     constexpr int CPR = D / 8;            // 16-byte chunks per K/V row
     constexpr int HT = 16 * NT;           // head columns per workgroup
-    constexpr int VSLOT = 32 * D * 2;     // bytes of one 32-row V slice
+    constexpr int VSLOT = 32 * D * 2;     // bytes of one 32-row K (or V) slice
+    constexpr int DV = D / DSPLIT;        // V columns this workgroup forms O for
+    constexpr int DTV = DV / 16;          // 16-wide d tiles of O^T
+    constexpr int FRV = DV / 16;          // 16-byte fragments per lane per V unit
+    constexpr int CPRV = DV / 8;          // 16-byte chunks per staged V row
+    static_assert(DSPLIT == 1 || DSPLIT == 2, "one or two workgroups per split");
     static_assert(UPP % KG == 0, "units must tile the phase");
     static_assert(BPP <= 32, "decision masks are 32-bit");
-    static_assert(W * DT * 4 * 64 * 4 <= NSLOT * W * VSLOT, "O reduction must fit the staging area");
+    static_assert(W * DTV * 4 * 64 * 4 <= NSLOT * W * VSLOT, "O reduction must fit the staging area");
     static_assert(NSLOT >= 2 && NSLOT <= 4, "staging ring depth");
 
     __shared__ __attribute__((aligned(16))) char lds_v[NSLOT * W * VSLOT];
     __shared__ float lds_pmax[2][UPP * HT];
     __shared__ float lds_l[W][64];
 
-    const int split = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
+    int split = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z, half = 0;
+    if constexpr (DSPLIT == 2) {
+        // 1-D grid: workgroups L and L + 8 form a pair (same unit, halves 0 and 1),
+        // so that both land on the same XCD (workgroups go round-robin over 8)
+        const int L = blockIdx.x;
+        const int unit = (L / 16) * 8 + (L % 8);
+        half = (L / 8) & 1;
+        if (unit >= a.S * a.Hkv * a.B) return;
+        split = unit % a.S;
+        hkv = (unit / a.S) % a.Hkv;
+        b = unit / (a.S * a.Hkv);
+    }
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int g = lane >> 4, n = lane & 15;
     // Row stride a.N (capacity); this sequence's context is its first N keys, nk
@@ -88,7 +108,7 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
 
     const uint16_t* kbase = a.k + ((size_t)b * a.Hkv + hkv) * (size_t)a.N * D;
     const uint16_t* vbase = a.v + ((size_t)b * a.Hkv + hkv) * (size_t)a.N * D;
-    if (a.lens && split == a.S - 1 && nk < a.nk) {
+    if (a.lens && split == a.S - 1 && nk < a.nk && half == 0) {
         // blocks past the sequence's end are not visited (2)
         for (int x = threadIdx.x; x < (G + 1) * (a.nk - nk); x += 64 * W) {
             const int r = x / (a.nk - nk), j = nk + x % (a.nk - nk);
@@ -113,14 +133,14 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
         }
     }
 
-    f32x4 oacc[NT][DT];
+    f32x4 oacc[NT][DTV];
     float m_run[NT], l_part[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         m_run[nt] = kNegInf;
         l_part[nt] = 0.f;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) oacc[nt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int dt = 0; dt < DTV; ++dt) oacc[nt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
     int parity = 0;
@@ -264,7 +284,7 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
         }
 
         // decision bytes: one lane per (head, block)
-        if (a.skip != nullptr) {
+        if (a.skip != nullptr && half == 0) {
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
                 const int h = nt * 16 + n;
@@ -273,7 +293,7 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
                 for (int bi = wave * 4 + g; bi < nb; bi += 4 * W) row[bi] = (uint8_t)(((keep[nt] >> bi) & 1u) ^ 1u);
             }
         }
-        if (a.vskip != nullptr) {
+        if (a.vskip != nullptr && half == 0) {
             uint8_t* row = a.vskip + ((size_t)b * a.Hkv + hkv) * a.nk + p0;
             for (int bi = threadIdx.x; bi < nb; bi += 64 * W) row[bi] = (uint8_t)(((vkeep >> bi) & 1u) ^ 1u);
         }
@@ -287,18 +307,22 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
         for (int u = 0; u < UW; ++u) km |= (uint32_t)kept[u] << u;
         km = (uint32_t)__builtin_amdgcn_readfirstlane((int)km);
+        // A V unit of DV columns fills 1/DSPLIT of a slot: the V ring holds VD =
+        // NSLOT * DSPLIT units per wave (more V copies in flight when each is smaller).
+        constexpr int VD = NSLOT * DSPLIT;
+        auto vslot_of = [&](int u) { return lds_v + NSLOT * wave * VSLOT + (u % VD) * (VSLOT / DSPLIT); };
         auto issue_v = [&](int u) {
-            const char* slot = slot_of(u);
+            const char* slot = vslot_of(u);
 #pragma unroll
-            for (int f = 0; f < FR; ++f) {
+            for (int f = 0; f < FRV; ++f) {
                 const int p = 64 * f + lane;
-                const int row = p / CPR, cc = (p % CPR) ^ (row & (CPR - 1));
+                const int row = p / CPRV, cc = (p % CPRV) ^ (row & (CPRV - 1));
                 const int key = min(ukey0[u] + row, N - 1);
-                global_to_lds16(vbase + (size_t)key * D + cc * 8, lds_addr(slot + 1024 * f));
+                global_to_lds16(vbase + (size_t)key * D + half * DV + cc * 8, lds_addr(slot + 1024 * f));
             }
         };
 #pragma unroll
-        for (int u = 0; u < (NSLOT < UW ? NSLOT : UW); ++u)
+        for (int u = 0; u < (VD < UW ? VD : UW); ++u)
             if ((km >> u) & 1u) issue_v(u);
 
         // rescale the running state to the phase's new max (overlaps the V loads)
@@ -306,16 +330,16 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
         for (int nt = 0; nt < NT; ++nt) {
             l_part[nt] *= alpha[nt];
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) oacc[nt][dt] *= alpha[nt];
+            for (int dt = 0; dt < DTV; ++dt) oacc[nt][dt] *= alpha[nt];
         }
 
 #pragma unroll
         for (int u = 0; u < UW; ++u) {
             if ((km >> u) & 1u) {
                 // V(u) is complete once only the kept units issued after it
-                // (among u + 1 .. u + NSLOT - 1) are outstanding
-                wait_vm<FR>(__builtin_popcount((km >> (u + 1)) & ((1u << (NSLOT - 1)) - 1u)));
-                const lds_char* vslot = (const lds_char*)slot_of(u);
+                // (among u + 1 .. u + VD - 1) are outstanding
+                wait_vm<FRV>(__builtin_popcount((km >> (u + 1)) & ((1u << (VD - 1)) - 1u)));
+                const lds_char* vslot = (const lds_char*)vslot_of(u);
                 const int blk_bit = (wave + W * u) / KG;
                 bf16x8 pf[NT];
 #pragma unroll
@@ -335,19 +359,19 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
                     pf[nt] = as_bf16x8(w4);
                 }
 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt) {
+                for (int dt = 0; dt < DTV; ++dt) {
                     const int cc = 2 * dt + ((n & 3) >> 1);
                     const int r0 = 4 * g + (n >> 2), r1 = 16 + 4 * g + (n >> 2);
-                    const u32x2 lo = lds_read_tr16(vslot + r0 * (2 * D) + ((cc ^ (r0 & (CPR - 1))) << 4) + (n & 1) * 8);
-                    const u32x2 hi = lds_read_tr16(vslot + r1 * (2 * D) + ((cc ^ (r1 & (CPR - 1))) << 4) + (n & 1) * 8);
+                    const u32x2 lo = lds_read_tr16(vslot + r0 * (2 * DV) + ((cc ^ (r0 & (CPRV - 1))) << 4) + (n & 1) * 8);
+                    const u32x2 hi = lds_read_tr16(vslot + r1 * (2 * DV) + ((cc ^ (r1 & (CPRV - 1))) << 4) + (n & 1) * 8);
                     const bf16x8 av = as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y});
 #pragma unroll
                     for (int nt = 0; nt < NT; ++nt) oacc[nt][dt] = mfma16x16x32(av, pf[nt], oacc[nt][dt]);
                 }
             }
-            if (u + NSLOT < UW && ((km >> (u + NSLOT < UW ? u + NSLOT : 0)) & 1u)) {
-                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // slot u % NSLOT has been read
-                issue_v(u + NSLOT);
+            if (u + VD < UW && ((km >> (u + VD < UW ? u + VD : 0)) & 1u)) {
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // unit u's place in the ring has been read
+                issue_v(u + VD);
             }
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -361,9 +385,9 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
     for (int nt = 0; nt < NT; ++nt) {
         const float l = wave_sum_xor32(wave_sum_xor16(l_part[nt]));
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+        for (int dt = 0; dt < DTV; ++dt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) red[((wave * DT + dt) * 4 + i) * 64 + lane] = oacc[nt][dt][i];
+            for (int i = 0; i < 4; ++i) red[((wave * DTV + dt) * 4 + i) * 64 + lane] = oacc[nt][dt][i];
         lds_l[wave][lane] = l;
         __syncthreads();
         float lt = 0.f;
@@ -373,18 +397,18 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
         if (h < G) {
             const size_t orow = ((size_t)b * a.Hq + (size_t)hkv * G + h) * a.S + split;
             const float inv = lt > 0.f ? 1.f / lt : 0.f;  // 0: a split with no block
-            for (int dt = wave; dt < DT; dt += W) {
+            for (int dt = wave; dt < DTV; dt += W) {
                 float o4[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     float x = 0.f;
 #pragma unroll
-                    for (int w = 0; w < W; ++w) x += red[((w * DT + dt) * 4 + i) * 64 + lane];
+                    for (int w = 0; w < W; ++w) x += red[((w * DTV + dt) * 4 + i) * 64 + lane];
                     o4[i] = x * inv;
                 }
-                *(f32x4*)(a.o_part + orow * D + 16 * dt + 4 * g) = f32x4{o4[0], o4[1], o4[2], o4[3]};
+                *(f32x4*)(a.o_part + orow * D + half * DV + 16 * dt + 4 * g) = f32x4{o4[0], o4[1], o4[2], o4[3]};
             }
-            if (wave == 0 && g == 0) a.lse_part[orow] = m_run[nt] * kLn2 + logf(lt);
+            if (wave == 0 && g == 0 && half == 0) a.lse_part[orow] = m_run[nt] * kLn2 + logf(lt);
         }
         __syncthreads();
     }
@@ -444,6 +468,15 @@ hipError_t launch_split(const DecodeArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// Two workgroups per split (each half of the V columns), pairs 8 apart in a 1-D grid.
+template <int D, int BC, int NT, int UW, int W, int NSLOT>
+hipError_t launch_split_pairs(const DecodeArgs& a, hipStream_t stream) {
+    const int64_t units = (int64_t)a.S * a.Hkv * a.B;
+    const dim3 grid((unsigned)(2 * ((units + 7) / 8) * 8));
+    hipLaunchKernelGGL((decode_split_kernel<D, BC, NT, UW, W, NSLOT, false, 2>), grid, dim3(64 * W), 0, stream, a);
+    return hipGetLastError();
+}
+
 // The margin pass reads K only; the four-wave shape keeps 128 KiB in flight.
 template <int D, int BC>
 hipError_t launch_margins_nt(const DecodeArgs& a, hipStream_t stream) {
@@ -458,6 +491,8 @@ hipError_t launch_split_nt(const DecodeArgs& a, hipStream_t stream) {
     // few workgroups (one per CU) eight waves x two slots measured faster; with
     // many, one wave per SIMD x four slots (the SIMD's second wave lags otherwise).
     if (a.G <= 16) {
+        // at most half a workgroup per CU: two workgroups per split, each the V pass of half the columns
+        if ((int64_t)a.S * a.Hkv * a.B <= 128) return launch_split_pairs<D, BC, 1, 8, 8, 2>(a, stream);
         if ((int64_t)a.S * a.Hkv * a.B <= 256) return launch_split<D, BC, 1, 8, 8, 2>(a, stream);
         return launch_split<D, BC, 1, 16, 4, 4>(a, stream);
     }
