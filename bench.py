@@ -368,55 +368,60 @@ def bench_prefill(args, lib, torch, W):
 
 
 def bench_mla(args, lib, torch, W):
-    """MLA decode split kernel at 32K context: time, HBM bytes (the cache rows are read once), the
-    executed FLOPs (S for every head and token; P V for the kept blocks of each head group) and the
-    roofline bound by both HBM and MFMA."""
+    """MLA decode split kernel at 32K context, with 64- and 32-token blocks: time, HBM bytes (the cache
+    rows are read once), the executed FLOPs (S for every head and token; P V for the kept blocks of each
+    head group) and the roofline bound by both HBM and MFMA."""
     w = W.MLA_CONFIGS["decode_mla_32k"]
     x = W.generate(w, parts=("q", "k"))
     q = dev(np.ascontiguousarray(x["q"][:, :, 0]))
     kvs = [dev(np.ascontiguousarray(x["k"][:, 0]))]
     kvs.append(kvs[0].clone())  # two copies, 604 MB: beyond the Infinity Cache
     del x
-    B, Hq, N, dqk, dv, Bc, S = w.B, w.Hq, w.T, w.d, w.dv, w.Bc, w.num_splits
-    nk = -(-N // Bc)
-    o_part = torch.empty((B, Hq, S, dv), dtype=torch.float32, device="cuda")
-    lse_part = torch.empty((B, Hq, S), dtype=torch.float32, device="cuda")
-    skip = torch.empty((B, Hq, nk), dtype=torch.uint8, device="cuda")
+    B, Hq, N, dqk, dv, S = w.B, w.Hq, w.T, w.d, w.dv, w.num_splits
     stream = torch.cuda.current_stream()
     P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
-    hg = 64 if (Hq % 64 == 0 and S * (Hq // 64) * B >= 256) else 32
-    out = {}
-    for lam in (0.0,) + tuple(w.lambdas):
-        args_ = [(P(q), P(kv), P(o_part), P(lse_part), P(skip), B, Hq, N, dqk, dv, Bc, ctypes.c_double(w.score_scale),
-                  ctypes.c_double(lam), S, ctypes.c_void_p(stream.cuda_stream)) for kv in kvs]
-        for i in range(4):
-            assert lib.blasst_decode_mla(*args_[i % 2]) == 0
-        torch.cuda.synchronize()
-        reps = 50
-        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s0.record(stream)
-        for i in range(reps):
-            assert lib.blasst_decode_mla(*args_[i % 2]) == 0
-        s1.record(stream)
-        torch.cuda.synchronize()
-        us = s0.elapsed_time(s1) * 1e3 / reps
-        sk = skip.cpu().numpy().astype(bool)                      # [B, Hq, nk]
-        group_kept = ~sk.reshape(B, Hq // hg, hg, nk).all(axis=2)  # P V formed for the group
-        rows = np.minimum(Bc, N - Bc * np.arange(nk))              # tokens per block
-        s_flops = 2.0 * dqk * N * Hq * B
-        pv_flops = 2.0 * dv * hg * float((group_kept * rows).sum())
-        by = B * N * dqk * 2 + B * Hq * dqk * 2 + B * Hq * S * (dv + 1) * 4 + B * Hq * nk
-        out["%g" % lam] = dict(us=round(us, 2), GBs=round(by / us / 1e3, 1),
-                               frac_of_hbm_peak=round(by / us / 1e3 / HBM_PEAK_GBS, 4),
-                               tflops_executed=round((s_flops + pv_flops) / us / 1e6, 1),
-                               block_sparsity=round(float(sk.mean()), 5),
-                               pv_skipped_fraction=round(1.0 - float(group_kept.mean()), 5))
-    dense = out["0"]["us"]
-    for v in out.values():
-        v["speedup_vs_lambda0"] = round(dense / v["us"], 4)
+    o_part = torch.empty((B, Hq, S, dv), dtype=torch.float32, device="cuda")
+    lse_part = torch.empty((B, Hq, S), dtype=torch.float32, device="cuda")
+    by_block = {}
+    for Bc in (w.Bc, 32):
+        nk = -(-N // Bc)
+        skip = torch.empty((B, Hq, nk), dtype=torch.uint8, device="cuda")
+        hg = 64 if (Bc == 32 or (Hq % 64 == 0 and S * (Hq // 64) * B >= 256)) else 32
+        out = {}
+        for lam in (0.0,) + tuple(w.lambdas):
+            args_ = [(P(q), P(kv), P(o_part), P(lse_part), P(skip), B, Hq, N, dqk, dv, Bc,
+                      ctypes.c_double(w.score_scale), ctypes.c_double(lam), S, ctypes.c_void_p(stream.cuda_stream))
+                     for kv in kvs]
+            for i in range(4):
+                assert lib.blasst_decode_mla(*args_[i % 2]) == 0
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(TRIALS):
+                s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                s0.record(stream)
+                for i in range(20):
+                    assert lib.blasst_decode_mla(*args_[i % 2]) == 0
+                s1.record(stream)
+                torch.cuda.synchronize()
+                ts.append(s0.elapsed_time(s1) * 1e3 / 20)
+            us = float(np.median(ts))
+            sk = skip.cpu().numpy().astype(bool)                      # [B, Hq, nk]
+            group_kept = ~sk.reshape(B, Hq // hg, hg, nk).all(axis=2)  # P V formed for the group
+            rows = np.minimum(Bc, N - Bc * np.arange(nk))              # tokens per block
+            s_flops = 2.0 * dqk * N * Hq * B
+            pv_flops = 2.0 * dv * hg * float((group_kept * rows).sum())
+            by = B * N * dqk * 2 + B * Hq * dqk * 2 + B * Hq * S * (dv + 1) * 4 + B * Hq * nk
+            out["%g" % lam] = dict(us=round(us, 2), us_min=round(min(ts), 2), us_max=round(max(ts), 2),
+                                   GBs=round(by / us / 1e3, 1), frac_of_hbm_peak=round(by / us / 1e3 / HBM_PEAK_GBS, 4),
+                                   tflops_executed=round((s_flops + pv_flops) / us / 1e6, 1),
+                                   block_sparsity=round(float(sk.mean()), 5),
+                                   pv_skipped_fraction=round(1.0 - float(group_kept.mean()), 5))
+        dense = out["0"]["us"]
+        for v in out.values():
+            v["speedup_vs_lambda0"] = round(dense / v["us"], 4)
+        by_block["Bc%d" % Bc] = dict(heads_per_workgroup=hg, by_lambda=out)
     by = B * N * dqk * 2
-    return dict(workload=w.name, B=B, Hq=Hq, d_qk=dqk, d_v=dv, context=N, Bc=Bc, num_splits=S,
-                heads_per_workgroup=hg, by_lambda=out,
+    return dict(workload=w.name, B=B, Hq=Hq, d_qk=dqk, d_v=dv, context=N, num_splits=S, by_block=by_block,
                 hbm_roofline_us=round(by / (HBM_PEAK_GBS * 1e3), 2),
                 mfma_roofline_us_dense=round(2.0 * (dqk + dv) * N * Hq * B / (MFMA_BF16_PEAK_TFLOPS * 1e6), 2))
 

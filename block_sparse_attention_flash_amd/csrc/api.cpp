@@ -276,7 +276,8 @@ BLASST_EXPORT blasst_status blasst_decode_mla(const void* q, const void* kv, flo
             return BLASST_ERR_INVALID_ARG;
         const int64_t nk = ((int64_t)N + Bc - 1) / Bc;
         if (num_splits < 1 || num_splits > nk) return BLASST_ERR_INVALID_ARG;
-        if (d_qk != 576 || d_v != 512 || Bc != 64 || Hq % 32 != 0) return BLASST_ERR_UNSUPPORTED;
+        if (d_qk != 576 || d_v != 512 || (Bc != 64 && Bc != 32) || Hq % (Bc == 32 ? 64 : 32) != 0)
+            return BLASST_ERR_UNSUPPORTED;
         if ((int64_t)B * Hq == 0) return BLASST_OK;  // nothing to do; pointers are not read
         if (!q || !kv || !o_part || !lse_part) return BLASST_ERR_INVALID_ARG;
         if (!aligned16(q) || !aligned16(kv) || !aligned16(o_part)) return BLASST_ERR_INVALID_ARG;
@@ -295,7 +296,7 @@ BLASST_EXPORT blasst_status blasst_decode_mla(const void* q, const void* kv, flo
         a.S = num_splits;
         a.score_scale = static_cast<float>(softmax_scale * kLog2e);
         a.thr = log2_threshold(lambda);
-        return from_hip(blasst::launch_decode_mla(a, reinterpret_cast<hipStream_t>(stream)));
+        return from_hip(blasst::launch_decode_mla(a, Bc, reinterpret_cast<hipStream_t>(stream)));
     } catch (...) {
         return BLASST_ERR_INTERNAL;
     }

@@ -39,7 +39,7 @@ struct PrefillArgs {
     bool dense = false;         // the kernel built without the skip test (every tile kept)
 };
 
-// MLA decode (absorbed latent form): 576-wide cache rows, value = the first 512 columns, Bc = 64.
+// MLA decode (absorbed latent form): 576-wide cache rows, value = the first 512 columns, Bc in {32, 64}.
 struct MlaArgs {
     const uint16_t* q;   // bf16 [B, Hq, 576]
     const uint16_t* kv;  // bf16 [B, N, 576]
@@ -52,7 +52,7 @@ struct MlaArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs& a, int d, int Bc, hipStream_t stream);
-hipError_t launch_decode_mla(const MlaArgs& a, hipStream_t stream);
+hipError_t launch_decode_mla(const MlaArgs& a, int Bc, hipStream_t stream);
 hipError_t launch_decode_combine(const float* o_part, const float* lse_part, float* o, float* lse, int rows,
                                  int d, int S, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, int d, int Bc, hipStream_t stream);

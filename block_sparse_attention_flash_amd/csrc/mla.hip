@@ -12,10 +12,12 @@
 // workgroup keeps it, and a skipping head's P is zero.
 //
 // One workgroup = 8 waves per (split, group of 16*NT heads, sequence); blocks
-// of 64 tokens.  Per block:
-//   copy     the block's 64 cache rows go HBM -> LDS (global_load_lds_dwordx4,
-//            whole rows per instruction), double-buffered: block j+1 is in
-//            flight while block j is computed.  Latent rows (1 KiB) are
+// of BCM = 64 or 32 tokens.  Per block:
+//   copy     the block's cache rows go HBM -> LDS (global_load_lds_dwordx4,
+//            whole rows per instruction) through a ring of NSTAGE blocks: block
+//            j + NSTAGE - 1 is issued when block j starts (2 x 72 KiB at 64
+//            tokens, 4 x 36 KiB at 32: the smaller blocks keep three blocks of
+//            rows in flight instead of one).  Latent rows (1 KiB) are
 //            XOR-swizzled by 16-byte chunk within groups of 16 chunks, rotary
 //            rows (128 B) within their 8 chunks.
 //   S^T      K Q^T on MFMA 16x16x32 bf16 (16 keys x 16 heads per tile, 18
@@ -37,7 +39,6 @@ namespace blasst {
 
 namespace {
 
-constexpr int MLA_BC = 64;
 constexpr int MLA_DN = 512;  // latent columns (the value)
 constexpr int MLA_DR = 64;   // rotary columns
 constexpr int MLA_DQK = MLA_DN + MLA_DR;
@@ -45,21 +46,30 @@ constexpr int MLA_DQK = MLA_DN + MLA_DR;
 // physical 16-byte chunk of logical chunk c in latent row r (XOR within groups of 16)
 __device__ __forceinline__ int nope_chunk(int c, int r) { return (c & ~15) | ((c & 15) ^ (r & 15)); }
 
-template <int NT>
+// BCM tokens per block; NSTAGE blocks staged in LDS (NSTAGE - 1 in flight
+// while one is computed): 2 x 72 KiB at BCM = 64, 4 x 36 KiB at BCM = 32.
+template <int NT, int BCM>
 __global__ __launch_bounds__(512) void mla_split_kernel(MlaArgs a) {
     constexpr int W = 8;
+    constexpr int MLA_BC = BCM;
+    constexpr int KTB = BCM / 16;                // 16-key tiles per block
     constexpr int WPH = W / NT;                  // S waves per head tile
-    constexpr int KPW = 4 / WPH;                 // 16-key tiles per S wave
+    constexpr int KPW = KTB / WPH;               // 16-key tiles per S wave
     constexpr int HG = 16 * NT;                  // heads per workgroup
     constexpr int NOPE_ROW = 2 * MLA_DN;         // 1024 B
     constexpr int ROPE_ROW = 2 * MLA_DR;         // 128 B
     constexpr int NOPE_TILE = MLA_BC * NOPE_ROW;
     constexpr int STAGE = NOPE_TILE + MLA_BC * ROPE_ROW;
-    constexpr int PROW = 2 * MLA_BC + 16;        // one head's P^T row: 64 bf16 + 16 B pad
+    constexpr int NSTAGE = BCM == 32 ? 4 : 2;
+    constexpr int PROW = 2 * MLA_BC + 16;        // one head's P^T row: BCM bf16 + 16 B pad
     constexpr int KSTEPS = MLA_DQK / 32;         // 18
+    constexpr int NOPE_PER_WAVE = BCM / W;       // latent rows (1 KiB copies) per wave per block
+    constexpr int ROPE_WAVES = BCM / 8;          // waves with one rotary copy (8 rows) per block
     static_assert(NT == 2 || NT == 4, "16*NT heads per workgroup, NT in {2, 4}");
+    static_assert(BCM == 64 || (BCM == 32 && NT == 4), "32-token blocks need 64 heads per workgroup");
+    static_assert(KPW >= 1, "every S wave owns at least one key tile");
 
-    __shared__ __attribute__((aligned(16))) char lds_kv[2][STAGE];
+    __shared__ __attribute__((aligned(16))) char lds_kv[NSTAGE][STAGE];
     __shared__ __attribute__((aligned(16))) char lds_p[HG * PROW];
     __shared__ float lds_pmax[WPH][HG];
     __shared__ float lds_l[WPH][HG];
@@ -93,49 +103,83 @@ __global__ __launch_bounds__(512) void mla_split_kernel(MlaArgs a) {
     }
     float l_part = 0.f;  // S role: row-sum partial of head 16*sht + n over this lane's keys
 
-    // Wave w copies rows 8w .. 8w + 7 of a block: one 1 KiB instruction per
-    // latent row (lane l lands at physical chunk l) and one for the 8 rotary
-    // rows (lane l -> row 8w + l/8, physical chunk l % 8).  Rows past the
-    // context re-read its last row.
+    // Wave w copies latent rows w, w + 8, ... of a block (one 1 KiB instruction
+    // per row, lane l landing at physical chunk l) and, for w < BCM/8, the 8
+    // rotary rows 8w .. 8w + 7 (lane l -> row 8w + l/8, physical chunk l % 8).
+    // Rows past the context re-read its last row.
+    const bool rope_wave = wave < ROPE_WAVES;
     auto issue = [&](int j, int stage) {
         char* base = &lds_kv[stage][0];
 #pragma unroll
-        for (int r8 = 0; r8 < 8; ++r8) {
-            const int r = 8 * wave + r8;
+        for (int i = 0; i < NOPE_PER_WAVE; ++i) {
+            const int r = wave + W * i;
             const int key = min(j * MLA_BC + r, N - 1);
             const int c = nope_chunk(lane, r);
             global_to_lds16(kvb + (size_t)key * MLA_DQK + 8 * c, lds_addr(base + r * NOPE_ROW));
         }
-        const int r = 8 * wave + (lane >> 3);
-        const int key = min(j * MLA_BC + r, N - 1);
-        const int c = (lane & 7) ^ (r & 7);
-        global_to_lds16(kvb + (size_t)key * MLA_DQK + MLA_DN + 8 * c, lds_addr(base + NOPE_TILE + 8 * wave * ROPE_ROW));
+        if (rope_wave) {
+            const int r = 8 * wave + (lane >> 3);
+            const int key = min(j * MLA_BC + r, N - 1);
+            const int c = (lane & 7) ^ (r & 7);
+            global_to_lds16(kvb + (size_t)key * MLA_DQK + MLA_DN + 8 * c,
+                            lds_addr(base + NOPE_TILE + 8 * wave * ROPE_ROW));
+        }
     };
+    // block j's copies are complete once only those of the nb blocks issued after it are outstanding
+    auto wait_blocks_after = [&](int nb) {
+        if (nb <= 0) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        } else if (nb == 1) {
+            if (rope_wave) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NOPE_PER_WAVE + 1) : "memory");
+            else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NOPE_PER_WAVE) : "memory");
+        } else {
+            if (rope_wave) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (NOPE_PER_WAVE + 1)) : "memory");
+            else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NOPE_PER_WAVE) : "memory");
+        }
+    };
+    static_assert(NSTAGE - 2 <= 2, "wait_blocks_after covers up to two blocks in flight");
 
-    if (j0 < j1) issue(j0, 0);
+#pragma unroll
+    for (int q = 0; q < NSTAGE - 1; ++q)
+        if (j0 + q < j1) issue(j0 + q, q);
     for (int j = j0; j < j1; ++j) {
-        const int st = (j - j0) & 1;
-        // this block's rows have landed (every wave's copies) and the previous
-        // block's P and stage are no longer read
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        const int st = (j - j0) % NSTAGE;
+        // this block's rows have landed (every wave's copies) and the stage the
+        // next copy goes to (block j - 1's) and the P buffer are no longer read
+        wait_blocks_after(min(NSTAGE - 2, j1 - 1 - j));
         __syncthreads();
-        if (j + 1 < j1) issue(j + 1, st ^ 1);
+        if (j + NSTAGE - 1 < j1) issue(j + NSTAGE - 1, (j + NSTAGE - 1 - j0) % NSTAGE);
         const char* kvt = &lds_kv[st][0];
 
-        // ---- S^T tiles of this wave
+        // ---- S^T tiles of this wave: fragment f = (k-step f / KPW, key tile f % KPW),
+        //      PFK fragments read ahead of the MFMA that consumes them
         f32x4 sacc[KPW];
 #pragma unroll
         for (int kk = 0; kk < KPW; ++kk) sacc[kk] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) {
-#pragma unroll
-            for (int kk = 0; kk < KPW; ++kk) {
+        {
+            constexpr int NF = KSTEPS * KPW, PFK = 8;
+            auto kread = [&](int f) -> u32x4 {
+                const int st_ = f / KPW, kk = f % KPW;
                 const int r = 16 * (kt0 + kk) + n;
-                const int c = 4 * (s < 16 ? s : s - 16) + g;
-                const int off = s < 16 ? r * NOPE_ROW + (nope_chunk(c, r) << 4)
-                                       : NOPE_TILE + r * ROPE_ROW + ((c ^ (r & 7)) << 4);
-                const u32x4 kf = *(const u32x4*)(kvt + off);
-                sacc[kk] = mfma16x16x32(as_bf16x8(kf), qf[s], sacc[kk]);
+                const int c = 4 * (st_ < 16 ? st_ : st_ - 16) + g;
+                const int off = st_ < 16 ? r * NOPE_ROW + (nope_chunk(c, r) << 4)
+                                         : NOPE_TILE + r * ROPE_ROW + ((c ^ (r & 7)) << 4);
+                return *(const u32x4*)(kvt + off);
+            };
+            u32x4 kf[PFK];
+#pragma unroll
+            for (int f = 0; f < PFK; ++f) kf[f] = kread(f);
+#pragma unroll
+            for (int f = 0; f < NF; ++f) {
+                const u32x4 cur = kf[f % PFK];
+                if (f + PFK < NF) kf[f % PFK] = kread(f + PFK);
+                sacc[f % KPW] = mfma16x16x32(as_bf16x8(cur), qf[f / KPW], sacc[f % KPW]);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, PFK, 0);
+#pragma unroll
+            for (int f = 0; f < NF; ++f) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (f + PFK < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
         }
         float pm = kNegInf;
@@ -208,7 +252,7 @@ __global__ __launch_bounds__(512) void mla_split_kernel(MlaArgs a) {
             for (int dd = 0; dd < 4; ++dd) oacc[nt][dd] *= alpha[nt];
         if (vkeep) {
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
+            for (int ks = 0; ks < MLA_BC / 32; ++ks) {
                 // B = P^T: k-slots 0..3 = keys 32ks + 4g + i, 4..7 = keys 32ks + 16 + 4g + i
                 bf16x8 pf[NT];
 #pragma unroll
@@ -258,13 +302,17 @@ __global__ __launch_bounds__(512) void mla_split_kernel(MlaArgs a) {
 
 }  // namespace
 
-hipError_t launch_decode_mla(const MlaArgs& a, hipStream_t stream) {
+hipError_t launch_decode_mla(const MlaArgs& a, int Bc, hipStream_t stream) {
+    if (Bc == 32) {  // 64 heads per workgroup (the caller checked Hq % 64 == 0)
+        hipLaunchKernelGGL((mla_split_kernel<4, 32>), dim3(a.S, a.Hq / 64, a.B), dim3(512), 0, stream, a);
+        return hipGetLastError();
+    }
     // 64 heads per workgroup when that still gives every CU a workgroup, else 32
     const bool wide = a.Hq % 64 == 0 && (int64_t)a.S * (a.Hq / 64) * a.B >= 256;
     if (wide) {
-        hipLaunchKernelGGL(mla_split_kernel<4>, dim3(a.S, a.Hq / 64, a.B), dim3(512), 0, stream, a);
+        hipLaunchKernelGGL((mla_split_kernel<4, 64>), dim3(a.S, a.Hq / 64, a.B), dim3(512), 0, stream, a);
     } else {
-        hipLaunchKernelGGL(mla_split_kernel<2>, dim3(a.S, a.Hq / 32, a.B), dim3(512), 0, stream, a);
+        hipLaunchKernelGGL((mla_split_kernel<2, 64>), dim3(a.S, a.Hq / 32, a.B), dim3(512), 0, stream, a);
     }
     return hipGetLastError();
 }

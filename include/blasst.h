@@ -185,10 +185,12 @@ blasst_status blasst_decode_ragged(const void* q, const void* k, const void* v, 
  *   softmax_scale  the model's scale (e.g. 1/sqrt(192) for 128 + 64 query
  *              columns before absorption); finite and > 0
  *   num_splits 1 <= num_splits <= ceil(N/Bc)
- * Built for d_qk = 576, d_v = 512, Bc = 64 and Hq a multiple of 32.
+ * Built for d_qk = 576, d_v = 512, and Bc = 64 with Hq a multiple of 32, or
+ * Bc = 32 with Hq a multiple of 64 (smaller blocks let the kernel keep three
+ * blocks of cache rows in flight instead of one).
  * Errors: INVALID_ARG for a null q/kv/o_part/lse_part, B/Hq < 0, N <= 0,
  * d_v > d_qk, a bad scale or lambda, bad num_splits, a misaligned pointer;
- * UNSUPPORTED for other d_qk/d_v/Bc or Hq not a multiple of 32.  Scalar
+ * UNSUPPORTED for other d_qk/d_v/Bc or head counts.  Scalar
  * arguments are checked first; then B*Hq == 0 returns OK and does nothing.
  */
 blasst_status blasst_decode_mla(const void* q, const void* kv, float* o_part, float* lse_part,

@@ -160,7 +160,8 @@ def decode_mla(lib, q=FAKE, kv=FAKE, B=2, Hq=128, N=4096, dqk=576, dv=512, Bc=64
     (dict(q=None), 1), (dict(kv=None), 1), (dict(kv=P(0x1004)), 1), (dict(N=0), 1), (dict(S=0), 1),
     (dict(S=65), 1), (dict(dv=600), 1), (dict(scale=0.0), 1), (dict(scale=float("inf")), 1),
     (dict(scale=float("nan")), 1), (dict(lam=1.0), 1), (dict(dqk=128, dv=128), 2), (dict(Bc=128), 2),
-    (dict(Hq=16), 2), (dict(Hq=48), 2), (dict(B=0), 0), (dict(Hq=0), 0),
+    (dict(Hq=16), 2), (dict(Hq=48), 2), (dict(Bc=32, Hq=96), 2), (dict(Bc=16), 2), (dict(B=0), 0),
+    (dict(Hq=0), 0), (dict(B=0, Bc=32), 0),
 ])
 def test_decode_mla_validation(lib, kw, status):
     assert decode_mla(lib, **kw) == status

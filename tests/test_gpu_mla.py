@@ -33,8 +33,8 @@ def say(*a):
     sys.stdout.flush()
 
 
-def mla_inputs(B, Hq, N, S, seed, hot=0.02):
-    w = W.Workload("t", "decode", B=B, Hq=Hq, Hkv=1, d=576, T=N, Bc=64, lambdas=(1e-3,), hot_rate=hot, seed=seed,
+def mla_inputs(B, Hq, N, S, seed, hot=0.02, Bc=64):
+    w = W.Workload("t", "decode", B=B, Hq=Hq, Hkv=1, d=576, T=N, Bc=Bc, lambdas=(1e-3,), hot_rate=hot, seed=seed,
                    window=128, num_splits=S, dv=512, scale=SCALE)
     x = W.generate(w, parts=("q", "k"))
     return np.ascontiguousarray(x["q"][:, :, 0]), np.ascontiguousarray(x["k"][:, 0])
@@ -49,29 +49,40 @@ MLA = [
 ]
 
 
-@pytest.mark.parametrize("shape", MLA, ids=lambda s: "B%d_Hq%d_N%d_S%d" % s)
+MLA32 = [
+    # B, Hq, N, S: 32-token blocks (64 heads per workgroup)
+    (2, 64, 1000, 3),     # ragged context, stage ring shorter than a split
+    (1, 64, 4096, 128),   # one block per split
+    (2, 128, 777, 2),     # ragged, two head groups
+    (4, 128, 8192, 16),
+]
+
+
+@pytest.mark.parametrize("shape,Bc", [(s, 64) for s in MLA] + [(s, 32) for s in MLA32],
+                         ids=lambda v: ("B%d_Hq%d_N%d_S%d" % v) if isinstance(v, tuple) else "Bc%d" % v)
 @pytest.mark.parametrize("lam", [0.0, 1e-3, 1e-1])
-def test_mla_small(shape, lam):
+def test_mla_small(shape, Bc, lam):
     B, Hq, N, S = shape
-    q, kv = mla_inputs(B, Hq, N, S, seed=900 + N)
+    q, kv = mla_inputs(B, Hq, N, S, seed=900 + N, Bc=Bc)
     units = None
     if B * Hq > 128:  # sample heads of every sequence (the oracle is the slow side)
         rng = np.random.default_rng(N)
         units = sorted(int(u) for u in rng.choice(B * Hq, size=96, replace=False))
-    rep = check_mla(q, kv, 64, lam, S, SCALE, 512, units=units)
-    say("mla", shape, lam, rep)
+    rep = check_mla(q, kv, Bc, lam, S, SCALE, 512, units=units)
+    say("mla", shape, "Bc", Bc, lam, rep)
 
 
-def test_mla_decode_mla_32k_sampled():
+@pytest.mark.parametrize("Bc", [64, 32])
+def test_mla_decode_mla_32k_sampled(Bc):
     w = W.MLA_CONFIGS["decode_mla_32k"]
     x = W.generate(w, parts=("q", "k"))
     q, kv = np.ascontiguousarray(x["q"][:, :, 0]), np.ascontiguousarray(x["k"][:, 0])
     del x
-    gpu = run_gpu_mla(to_device(q), to_device(kv), w.Bc, w.lambdas[0], w.num_splits, w.score_scale, w.dv)
+    gpu = run_gpu_mla(to_device(q), to_device(kv), Bc, w.lambdas[0], w.num_splits, w.score_scale, w.dv)
     rng = np.random.default_rng(11)
     units = sorted(int(u) for u in rng.choice(w.B * w.Hq, size=64, replace=False))
-    rep = check_mla(q, kv, w.Bc, w.lambdas[0], w.num_splits, w.score_scale, w.dv, units=units, gpu=gpu)
-    say("decode_mla_32k sampled", rep, "block sparsity %.4f" % float(gpu["skip"].mean()))
+    rep = check_mla(q, kv, Bc, w.lambdas[0], w.num_splits, w.score_scale, w.dv, units=units, gpu=gpu)
+    say("decode_mla_32k sampled Bc", Bc, rep, "block sparsity %.4f" % float(gpu["skip"].mean()))
 
 
 def test_mla_deterministic_and_dense_equal_lambda_zero():
