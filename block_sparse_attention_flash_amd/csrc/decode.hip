@@ -77,6 +77,17 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
     static_assert(BPP <= 32, "decision masks are 32-bit");
     static_assert(W * DTV * 4 * 64 * 4 <= NSLOT * W * VSLOT, "O reduction must fit the staging area");
     static_assert(NSLOT >= 2 && NSLOT <= 4, "staging ring depth");
+    // Early V (pairs with a two-slot ring): the blocks whose units every wave has
+    // finished before its last two K units arrive are decided at that point, and
+    // the V copies of the wave's first VD units go into the slots those two K
+    // units free, so the V stream is already running when the K pass ends.
+    constexpr int VD = NSLOT * DSPLIT;    // V units in the ring (a V unit fills 1/DSPLIT slot)
+    constexpr bool EARLYV = !MARGINS && DSPLIT == 2 && NSLOT == 2 && UW >= 4;
+    constexpr int UE = UW - 2;            // K units consumed before the early decisions
+    constexpr int BE = EARLYV ? W * UE / KG : 0;  // blocks decided early
+    constexpr int BG = BPP < 4 ? BPP : 4;  // blocks per group of LDS reads in the decisions
+    static_assert(!EARLYV || (UE % NSLOT == 0 && W * UE % KG == 0 && BE % BG == 0 && W * VD <= KG * BE),
+                  "the ring's first V units must lie in blocks decided early");
 
     __shared__ __attribute__((aligned(16))) char lds_v[NSLOT * W * VSLOT];
     __shared__ float lds_pmax[2][UPP * HT];
@@ -178,12 +189,93 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
         for (int u = 0; u < (NSLOT < UW ? NSLOT : UW); ++u) issue_k(u);
 
+        // ---- decisions (prefix max of the block maxima; no cascade): blocks
+        //      [lo, hi) of the phase, continuing the running max m_dec
+        float m_dec[NT];
+        uint32_t keep[NT];
+        float vmax_blk[MARGINS ? BPP : 1];
+#pragma unroll
+        for (int bi = 0; bi < (MARGINS ? BPP : 1); ++bi) vmax_blk[bi] = kNegInf;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            m_dec[nt] = m_run[nt];
+            keep[nt] = 0u;
+        }
+        auto decide = [&](int lo, int hi) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                // block maxima four blocks at a time: each group's LDS reads go out together
+                float m = m_dec[nt];
+                uint32_t kb = keep[nt];
+#pragma unroll
+                for (int b0 = lo; b0 < hi; b0 += BG) {
+                    float bmv[BG];
+#pragma unroll
+                    for (int bb = 0; bb < BG; ++bb) {
+                        float bm = kNegInf;
+#pragma unroll
+                        for (int kg = 0; kg < KG; ++kg)
+                            bm = fmaxf(bm, lds_pmax[parity][((b0 + bb) * KG + kg) * HT + nt * 16 + n]);
+                        bmv[bb] = bm;
+                    }
+#pragma unroll
+                    for (int bb = 0; bb < BG; ++bb) {
+                        const int bi = b0 + bb;
+                        if (bi < nb) {
+                            const float bm = bmv[bb];
+                            m = fmaxf(m, bm);
+                            kb |= (uint32_t)(!((bm - m) < a.thr)) << bi;
+                            if constexpr (MARGINS) {
+                                const float dm = head_ok[nt] ? (bm - m) * kLn2 : kNegInf;
+                                if (wave == 0 && g == 0 && head_ok[nt])
+                                    a.margin[((size_t)b * a.Hq + (size_t)hkv * G + nt * 16 + n) * a.nk + p0 + bi] = dm;
+                                if (a.vmargin != nullptr) vmax_blk[bi] = fmaxf(vmax_blk[bi], row16_max(dm));
+                            }
+                        }
+                    }
+                }
+                m_dec[nt] = m;
+                keep[nt] = head_ok[nt] ? kb : 0u;
+            }
+        };
+        auto vslot_of = [&](int u) { return lds_v + NSLOT * wave * VSLOT + (u % VD) * (VSLOT / DSPLIT); };
+        auto issue_v = [&](int u) {
+            const char* slot = vslot_of(u);
+#pragma unroll
+            for (int f = 0; f < FRV; ++f) {
+                const int p = 64 * f + lane;
+                const int row = p / CPRV, cc = (p % CPRV) ^ (row & (CPRV - 1));
+                const int key = min(ukey0[u] + row, N - 1);
+                global_to_lds16(vbase + (size_t)key * D + half * DV + cc * 8, lds_addr(slot + 1024 * f));
+            }
+        };
+        // this wave's kept units among the first VD (known after the early decisions)
+        uint32_t km_early = 0;
+
         f32x4 t[UW][2][NT];
 #pragma unroll
         for (int u = 0; u < UW; ++u) {
-            // K(u) is complete once only the copies of the units issued after it
-            // (u + 1 .. u + NSLOT - 1) are outstanding
-            wait_vm<FR>(min(NSLOT - 1, UW - 1 - u));
+            if constexpr (EARLYV) {
+                if (u == UE) {
+                    // every wave has published the maxima of its units 0 .. UE - 1,
+                    // which cover blocks 0 .. BE - 1
+                    __syncthreads();
+                    decide(0, BE);
+                    uint32_t vk = 0;
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) vk |= keep[nt];
+                    vk = row16_or(vk);
+#pragma unroll
+                    for (int v = 0; v < VD; ++v)
+                        km_early |= (uint32_t)(uok[v] && ((vk >> ((wave + W * v) / KG)) & 1u)) << v;
+                    km_early = (uint32_t)__builtin_amdgcn_readfirstlane((int)km_early);
+                }
+            }
+            // K(u) is complete once only the copies issued after it are outstanding:
+            // the K units u + 1 .. u + NSLOT - 1, and (early V) the V units issued
+            // into the slot K(UE) freed
+            if (EARLYV && u == UE + 1) wait_vm<FRV>(__builtin_popcount(km_early & ((1u << DSPLIT) - 1u)));
+            else wait_vm<FR>(min(NSLOT - 1, UW - 1 - u));
             const char* kslot = slot_of(u);
             u32x4 kf[2][DS];
 #pragma unroll
@@ -195,6 +287,14 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
                 }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this slot has been read
             if (u + NSLOT < UW) issue_k(u + NSLOT);
+            if constexpr (EARLYV) {
+                // the slot K(u) used holds V units (u % NSLOT) * DSPLIT .. + DSPLIT - 1 of the ring
+                if (u >= UE) {
+#pragma unroll
+                    for (int v = 0; v < VD; ++v)
+                        if (v / DSPLIT == u % NSLOT && ((km_early >> v) & 1u)) issue_v(v);
+                }
+            }
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
                 float pm = kNegInf;
@@ -227,51 +327,15 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
         }
         __syncthreads();
 
-        // ================= decide (prefix max; no cascade) =================
-        uint32_t keep[NT];
+        // ================= decide (the blocks not decided early) =================
+        decide(BE, BPP);
         uint32_t vkeep = 0;
         float alpha[NT];
-        float vmax_blk[MARGINS ? BPP : 1];
-#pragma unroll
-        for (int bi = 0; bi < (MARGINS ? BPP : 1); ++bi) vmax_blk[bi] = kNegInf;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-            // block maxima four blocks at a time: each group's LDS reads go out together
-            float m = m_run[nt];
-            uint32_t kb = 0;
-            constexpr int BG = BPP < 4 ? BPP : 4;
-#pragma unroll
-            for (int b0 = 0; b0 < BPP; b0 += BG) {
-                float bmv[BG];
-#pragma unroll
-                for (int bb = 0; bb < BG; ++bb) {
-                    float bm = kNegInf;
-#pragma unroll
-                    for (int kg = 0; kg < KG; ++kg)
-                        bm = fmaxf(bm, lds_pmax[parity][((b0 + bb) * KG + kg) * HT + nt * 16 + n]);
-                    bmv[bb] = bm;
-                }
-#pragma unroll
-                for (int bb = 0; bb < BG; ++bb) {
-                    const int bi = b0 + bb;
-                    if (bi < nb) {
-                        const float bm = bmv[bb];
-                        m = fmaxf(m, bm);
-                        kb |= (uint32_t)(!((bm - m) < a.thr)) << bi;
-                        if constexpr (MARGINS) {
-                            const float dm = head_ok[nt] ? (bm - m) * kLn2 : kNegInf;
-                            if (wave == 0 && g == 0 && head_ok[nt])
-                                a.margin[((size_t)b * a.Hq + (size_t)hkv * G + nt * 16 + n) * a.nk + p0 + bi] = dm;
-                            if (a.vmargin != nullptr) vmax_blk[bi] = fmaxf(vmax_blk[bi], row16_max(dm));
-                        }
-                    }
-                }
-            }
-            kb = head_ok[nt] ? kb : 0u;
-            keep[nt] = kb;
-            vkeep |= kb;
-            alpha[nt] = head_ok[nt] ? exp2_fast(m_run[nt] - m) : 1.f;
-            m_run[nt] = head_ok[nt] ? m : m_run[nt];
+            vkeep |= keep[nt];
+            alpha[nt] = head_ok[nt] ? exp2_fast(m_run[nt] - m_dec[nt]) : 1.f;
+            m_run[nt] = head_ok[nt] ? m_dec[nt] : m_run[nt];
         }
         vkeep = row16_or(vkeep);
         if constexpr (MARGINS) {
@@ -309,21 +373,12 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
         km = (uint32_t)__builtin_amdgcn_readfirstlane((int)km);
         // A V unit of DV columns fills 1/DSPLIT of a slot: the V ring holds VD =
         // NSLOT * DSPLIT units per wave (more V copies in flight when each is smaller).
-        constexpr int VD = NSLOT * DSPLIT;
-        auto vslot_of = [&](int u) { return lds_v + NSLOT * wave * VSLOT + (u % VD) * (VSLOT / DSPLIT); };
-        auto issue_v = [&](int u) {
-            const char* slot = vslot_of(u);
+        // With early V the ring's first VD units are already on their way.
+        if constexpr (!EARLYV) {
 #pragma unroll
-            for (int f = 0; f < FRV; ++f) {
-                const int p = 64 * f + lane;
-                const int row = p / CPRV, cc = (p % CPRV) ^ (row & (CPRV - 1));
-                const int key = min(ukey0[u] + row, N - 1);
-                global_to_lds16(vbase + (size_t)key * D + half * DV + cc * 8, lds_addr(slot + 1024 * f));
-            }
-        };
-#pragma unroll
-        for (int u = 0; u < (VD < UW ? VD : UW); ++u)
-            if ((km >> u) & 1u) issue_v(u);
+            for (int u = 0; u < (VD < UW ? VD : UW); ++u)
+                if ((km >> u) & 1u) issue_v(u);
+        }
 
         // rescale the running state to the phase's new max (overlaps the V loads)
 #pragma unroll
