@@ -112,6 +112,7 @@ DECODE = [
     (3, 32, 8, 4096, 128, 128, 16, 128, [4096, 1500, 129]),    # 16 splits over 2 blocks
     (2, 64, 1, 2000, 128, 128, 3, 0, [1, 2000]),               # MQA, a single key
     (4, 16, 1, 1536, 128, 64, 8, 0, [1536, 700, 300, 1]),
+    (2, 8, 2, 40960, 128, 128, 8, 256, [40960, 23000]),      # paired workgroups, several phases per split
 ]
 
 
