@@ -8,28 +8,33 @@
 // kept blocks.  Here a batch ("phase") is as large as the registers allow
 // (for 4-head groups at Bc = 128: 16 blocks, a whole 32K/16-way split).
 //
-// One workgroup = W waves per (batch b, kv head, split).  Each block is cut
-// into 32-key units; wave w owns units w, w+W, w+2W, ... of the phase.
+// One workgroup = W waves per (batch b, kv head, split), or two per split
+// (DSPLIT = 2, each forming O for half of the d columns) when one per split
+// would leave CUs idle.  Each block is cut into 32-key units; wave w owns units
+// w, w+W, w+2W, ... of the phase.
 //
-//  K pass   every unit's K rows go straight from HBM into the MFMA A layout
-//           (16 bytes per lane) through a small register ring, so loads for
-//           later units are in flight while earlier ones are multiplied.
-//           S^T = K q^T runs on MFMA 16x16x32 bf16 with the 32 keys as two
-//           16-row tiles and the G query heads of the group as 16-wide
-//           column tiles (heads beyond G are zero columns that never vote).
-//           The S^T tiles stay in registers; each unit's per-head partial
-//           max goes to LDS.
-//  decide   one barrier; every lane then walks the phase's blocks in order.
+//  K pass   every unit's 32 K rows go HBM -> LDS (global_load_lds_dwordx4,
+//           whole rows per instruction, XOR-swizzled by 16-byte chunk) through
+//           a ring of NSLOT slots per wave, so copies for later units are in
+//           flight while earlier ones are multiplied; they are read back in the
+//           MFMA A layout (ds_read_b128).  S^T = K q^T runs on MFMA 16x16x32
+//           bf16 with the 32 keys as two 16-row tiles and the G query heads of
+//           the group as 16-wide column tiles (heads beyond G are zero columns
+//           that never vote).  The S^T tiles stay in registers; each unit's
+//           per-head partial max goes to LDS.
+//  decide   a barrier; every lane then walks the phase's blocks in order.
 //           Because a skipped block never moves the running max
 //           (mt < m + ln(lambda) < m), the running max before block j is the
 //           prefix max of the block maxima: all decisions of the phase are
 //           taken at once with no cascade.  V is needed for a block iff some
-//           head of the group keeps it.
-//  V pass   only kept units: V rows go HBM -> LDS (global_load_lds_dwordx4,
-//           pre-swizzled addresses) through a two-slot ring per wave, and are
-//           read back transposed (ds_read_b64_tr_b16) as the A operand of
-//           O^T += V^T P^T.  P^T is the S^T accumulator (same lane layout)
-//           after 2^(t - m), rounded to bf16.
+//           head of the group keeps it.  With paired workgroups the blocks
+//           every wave has finished before its last two K units arrive are
+//           decided first, and their V copies start in the slots those two
+//           units free (early V).
+//  V pass   only kept units: V rows (or half rows) go HBM -> LDS through the
+//           same slots and are read back transposed (ds_read_b64_tr_b16) as
+//           the A operand of O^T += V^T P^T.  P^T is the S^T accumulator (same
+//           lane layout) after 2^(t - m), rounded to bf16.
 // Scores are kept in log2 units (t = s * log2(e)), so P uses v_exp_f32 directly
 // and the test reads t~ - m < ln(lambda) * log2(e).
 #include "device_common.h"
