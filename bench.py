@@ -386,7 +386,7 @@ def bench_mla(args, lib, torch, W):
     for Bc in (w.Bc, 32):
         nk = -(-N // Bc)
         skip = torch.empty((B, Hq, nk), dtype=torch.uint8, device="cuda")
-        hg = 64 if (Bc == 32 or (Hq % 64 == 0 and S * (Hq // 64) * B >= 256)) else 32
+        hg = 64 if Hq % 64 == 0 else 32
         out = {}
         for lam in (0.0,) + tuple(w.lambdas):
             args_ = [(P(q), P(kv), P(o_part), P(lse_part), P(skip), B, Hq, N, dqk, dv, Bc,
