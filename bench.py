@@ -80,6 +80,9 @@ def parse():
     p.add_argument("--prefill-reps", type=int, default=5, help="launches per prefill timing trial")
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-mla", action="store_true")
+    p.add_argument("--all-configs", action="store_true",
+                   help="also time every workload configuration (prefill_1k_tiny, decode_128k_b16, decode_mqa_16k "
+                        "besides the two 32K ones): time, fraction of the roofline, block sparsity")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--profile-target", choices=["decode", "prefill", "copy"], default=None,
@@ -367,6 +370,90 @@ def bench_prefill(args, lib, torch, W):
                 hbm_traffic_bytes_per_launch=measured_traffic("prefill_kernel", w.name))
 
 
+def bench_config(name, args, lib, torch, W):
+    """One workload configuration at its own lambda: a decode step (split + combine) or a prefill launch,
+    median of TRIALS trials, with the roofline fraction on the work done and the block sparsity."""
+    w = W.CONFIGS[name]
+    lam = w.lambdas[0]
+    x = W.generate(w)
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    f32 = dict(dtype=torch.float32, device="cuda")
+    B, Hq, T, d, Bc = w.B, w.Hq, w.T, w.d, w.Bc
+    nk = -(-T // Bc)
+
+    def trials(fns, reps):
+        for f in fns[:2]:
+            f()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(TRIALS):
+            s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s0.record(stream)
+            for i in range(reps):
+                fns[i % len(fns)]()
+            s1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(s0.elapsed_time(s1) / reps)
+        return float(np.median(ts)), min(ts), max(ts)
+
+    def ok(st):
+        if st != 0:
+            raise RuntimeError("libblasst call failed with status %d" % st)
+
+    if w.kind == "prefill":
+        xd = {k: dev(v) for k, v in x.items()}
+        o = torch.empty((B, Hq, T, d), **f32)
+        lse = torch.empty((B, Hq, T), **f32)
+        mask = torch.empty((B, Hq, nk, nk), dtype=torch.uint8, device="cuda")
+        a = (P(xd["q"]), P(xd["k"]), P(xd["v"]), P(o), P(lse), P(mask), B, Hq, T, d, w.G, Bc, ctypes.c_double(lam), 1, sp)
+        ms, lo, hi = trials([lambda: ok(lib.blasst_prefill(*a))], max(args.prefill_reps, 20))
+        m = mask.cpu().numpy()
+        visited = B * Hq * nk * (nk + 1) // 2
+        skipped = int((m == 1).sum())
+        flops = (2 * visited - skipped) * 2.0 * Bc * Bc * d
+        tf = flops / (ms * 1e-3) / 1e12
+        return dict(kind="prefill", lam=lam, ms=round(ms, 4), ms_min=round(lo, 4), ms_max=round(hi, 4),
+                    tflops_executed=round(tf, 2), frac_of_mfma_peak=round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                    block_sparsity=round(skipped / visited, 5))
+    S = w.num_splits
+    footprint = 2 * x["k"].nbytes
+    ncopy = max(1, min(args.copies, int(np.ceil(600e6 / footprint))))
+    xs = [{k: dev(v) for k, v in x.items()} for _ in range(ncopy)]
+    del x
+    o_part = torch.empty((B, Hq, S, d), **f32)
+    lse_part = torch.empty((B, Hq, S), **f32)
+    o = torch.empty((B, Hq, d), **f32)
+    lse = torch.empty((B, Hq), **f32)
+    skip = torch.empty((B, Hq, nk), dtype=torch.uint8, device="cuda")
+    vskip = torch.empty((B, w.Hkv, nk), dtype=torch.uint8, device="cuda")
+    comb = (P(o_part), P(lse_part), P(o), P(lse), B, Hq, d, S, sp)
+    sargs = [(P(c["q"]), P(c["k"]), P(c["v"]), P(o_part), P(lse_part), P(skip), P(vskip), B, Hq, T, d, w.G, Bc,
+              ctypes.c_double(lam), 1, S, sp) for c in xs]
+
+    def step(a):
+        return lambda: (ok(lib.blasst_decode(*a)), ok(lib.blasst_decode_combine(*comb)))
+
+    def split(a):
+        return lambda: ok(lib.blasst_decode(*a))
+
+    reps = 200 if footprint < 1e9 else 20
+    step_ms, _, _ = trials([step(a) for a in sargs], reps)
+    split_ms, lo, hi = trials([split(a) for a in sargs], reps)
+    ok(lib.blasst_decode(*sargs[0]))
+    torch.cuda.synchronize()
+    sk, vsk = skip.cpu().numpy(), vskip.cpu().numpy()
+    by = decode_bytes(w, vsk)
+    gbs = by["split"] / (split_ms * 1e-3) / 1e9
+    return dict(kind="decode", lam=lam, step_us=round(step_ms * 1e3, 2), split_kernel_us=round(split_ms * 1e3, 2),
+                split_kernel_us_min=round(lo * 1e3, 2), split_kernel_us_max=round(hi * 1e3, 2),
+                split_GBs=round(gbs, 1), frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4),
+                step_GBs=round((by["split"] + by["combine"]) / (step_ms * 1e-3) / 1e9, 1),
+                bytes_per_split_launch=by["split"], kv_copies_rotated=ncopy,
+                block_sparsity=round(float(sk.mean()), 5), vload_sparsity=round(float(vsk.mean()), 5))
+
+
 def bench_mla(args, lib, torch, W):
     """MLA decode split kernel at 32K context, with 64- and 32-token blocks: time, HBM bytes (the cache
     rows are read once), the executed FLOPs (S for every head and token; P V for the kept blocks of each
@@ -495,6 +582,12 @@ def main():
     d = bench_decode(args, lib, torch, W)
     pre = None if args.no_prefill else bench_prefill(args, lib, torch, W)
     mla = None if args.no_mla else bench_mla(args, lib, torch, W)
+    configs = None
+    if args.all_configs:
+        configs = {}
+        for name in ("prefill_1k_tiny", "decode_128k_b16", "decode_mqa_16k"):
+            configs[name] = bench_config(name, args, lib, torch, W)
+            torch.cuda.empty_cache()
     cpu = None if args.no_cpu_baseline else cpu_baseline(args, d)
 
     by = d["bytes"]
@@ -536,6 +629,7 @@ def main():
                    "bytes": by},
         "prefill": pre,
         "mla_decode": mla,
+        "other_configs": configs,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
