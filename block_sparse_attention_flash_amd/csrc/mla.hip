@@ -45,8 +45,18 @@ constexpr int MLA_DN = 512;  // latent columns (the value)
 constexpr int MLA_DR = 64;   // rotary columns
 constexpr int MLA_DQK = MLA_DN + MLA_DR;
 
-// physical 16-byte chunk of logical chunk c in latent row r (XOR within groups of 16)
-__device__ __forceinline__ int nope_chunk(int c, int r) { return (c & ~15) | ((c & 15) ^ (r & 15)); }
+// Physical 16-byte chunk of logical chunk c in latent row r: an XOR within each
+// group of 16 chunks (256 B) by a GF(2)-linear image of the row's low four bits
+// (bits 0..3 -> masks 3, 6, 9, 8).  Measured (SQ_LDS_BANK_CONFLICT on an
+// in-bounds probe of both read patterns) to leave the S K reads (ds_read_b128,
+// lane (n, g): row 16 kt + n, chunk 4 st + g) and the P V transposed reads
+// (ds_read_b64_tr_b16, lane (n, g): rows 4 g + n / 4 and + 16, chunk
+// 2 dt + (n & 3) / 2) free of bank conflicts; the plain XOR by the row costs the
+// transposed reads a 2-way conflict.
+__device__ __forceinline__ int nope_chunk(int c, int r) {
+    const int f = ((r & 1) * 3) ^ (((r >> 1) & 1) * 6) ^ (((r >> 2) & 1) * 9) ^ (((r >> 3) & 1) * 8);
+    return (c & ~15) | ((c & 15) ^ f);
+}
 
 // BCM tokens per block; NSTAGE blocks staged in LDS (NSTAGE - 1 in flight
 // while one is computed): 2 x 72 KiB at BCM = 64, 4 x 36 KiB at BCM = 32.
