@@ -341,7 +341,11 @@ __global__ __launch_bounds__(512) void mla_pipe_kernel(MlaArgs a) {
     // P^T of a sub-block (32 keys per head) lives in buffer u % NPH from the end
     // of its block's decision step until its P V step u + HPB
     constexpr int NPH = HPB == 1 ? 2 : 3;
-    constexpr int PROW = HPB == 1 ? 2 * SB + 16 : 2 * SB + 8;  // one head's P^T row: 32 bf16 + pad (8 B: three buffers just fit)
+    // One head's P^T row of a sub-block: 32 bf16 in k-slot order (bytes 16 g .. 16 g + 15 hold
+    // keys 4 g .. 4 g + 3 and 16 + 4 g .. 16 + 4 g + 3, the B fragment of lane group g), written
+    // and read 16 bytes per lane.  Row strides measured bank-conflict free for that pattern
+    // (96 B) or, where three buffers must fit (64-token blocks), the one with the fewest (64 B).
+    constexpr int PROW = HPB == 1 ? 96 : 64;
     static_assert(BCM == 32 || BCM == 64, "32- or 64-token blocks");
     static_assert(NSTAGE * STAGE + NPH * HG * PROW + 2 * HG * 4 * 2 + 2 * 4 * 4 <= 160 * 1024, "LDS budget");
 
@@ -484,17 +488,17 @@ __global__ __launch_bounds__(512) void mla_pipe_kernel(MlaArgs a) {
             if (a.skip != nullptr && g == 0) a.skip[((size_t)b * a.Hq + h0 + 16 * wave + n) * nk + jb] = (uint8_t)!keep;
             const int u0 = t - (HPB - 1);  // the block's first sub-block
 #pragma unroll
-            for (int kt = 0; kt < 2 * HPB; ++kt) {
-                float p[4];
+            for (int sb = 0; sb < HPB; ++sb) {
+                float p[8];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float e = exp2_fast(sacc[kt][i] - m_run);
+                for (int i = 0; i < 8; ++i) {
+                    const float e = exp2_fast(sacc[2 * sb + i / 4][i % 4] - m_run);
                     p[i] = keep ? e : 0.f;
                 }
-                l_part += (p[0] + p[1]) + (p[2] + p[3]);
-                const u32x2 w2 = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
-                char* pbuf = &lds_p[(u0 + kt / 2) % NPH][0];
-                *(u32x2*)(pbuf + (16 * wave + n) * PROW + 2 * (16 * (kt % 2) + 4 * g)) = w2;
+                l_part += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+                char* prow = &lds_p[(u0 + sb) % NPH][0] + (16 * wave + n) * PROW + 16 * g;
+                *(u32x4*)prow = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                                      pack_bf16x2(p[6], p[7])};
             }
             const int par = (t / HPB) & 1;
             if (g == 0) lds_alpha[par][16 * wave + n] = alpha;
@@ -548,10 +552,7 @@ __global__ __launch_bounds__(512) void mla_pipe_kernel(MlaArgs a) {
             const char* pbuf = &lds_p[(u + NPH) % NPH][0];
             auto p_frag = [&](int nt) -> bf16x8 {
                 // B = P^T: k-slots 0..3 = keys 4 g + i, 4..7 = keys 16 + 4 g + i of the sub-block
-                const char* prow = pbuf + (16 * nt + n) * PROW + 2 * (4 * g);
-                const u32x2 lo = *(const u32x2*)prow;
-                const u32x2 hi = *(const u32x2*)(prow + 32);
-                return as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y});
+                return as_bf16x8(*(const u32x4*)(pbuf + (16 * nt + n) * PROW + 16 * g));
             };
             if constexpr (HPB == 1) {
                 // 32-token blocks: every LDS read of the step (V^T of sub-block t, the
