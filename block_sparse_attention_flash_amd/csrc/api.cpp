@@ -82,7 +82,7 @@ blasst_status decode_impl(const void* q, const void* k, const void* v, float* o_
         const int64_t nk = ((int64_t)N + Bc - 1) / Bc;
         if (num_splits < 1 || num_splits > nk) return BLASST_ERR_INVALID_ARG;
         if (!supported_dim(d) || !supported_dim(Bc)) return BLASST_ERR_UNSUPPORTED;
-        if (gqa_ratio > 64) return BLASST_ERR_UNSUPPORTED;  // one workgroup covers at most 64 heads of a group
+        if (gqa_ratio > 128) return BLASST_ERR_UNSUPPORTED;  // at most four 32-head workgroups per split
         if ((int64_t)B * Hq == 0) return BLASST_OK;  // nothing to do; pointers are not read
         if (!q || !k || !v || !o_part || !lse_part) return BLASST_ERR_INVALID_ARG;
         if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o_part)) return BLASST_ERR_INVALID_ARG;

@@ -39,6 +39,7 @@
 // and the test reads t~ - m < ln(lambda) * log2(e).
 #include "device_common.h"
 #include "kernels.h"
+#include <climits>
 
 namespace blasst {
 
@@ -62,7 +63,12 @@ __device__ __forceinline__ void wait_vm(int n) {
 // of the d columns; both run the same K pass and decisions (the second one's
 // K reads hit the L2 the first one filled: the pair sits on one XCD), so each
 // CU streams K plus half of V instead of K plus all of V.
-template <int D, int BC, int NT, int UW, int W, int NSLOT, bool MARGINS = false, int DSPLIT = 1>
+// HS > 1: HS workgroups per split, each the whole pass for HT = 16 NT of the
+// group's heads (a group wider than one workgroup's registers hold); they sit
+// on one XCD, so the K and V blocks they share come from HBM once.  The V skip
+// mask is then an OR of the parts' "loaded" votes: the launcher sets it to
+// "not loaded" first and each part clears the bytes of the blocks it loads.
+template <int D, int BC, int NT, int UW, int W, int NSLOT, bool MARGINS = false, int DSPLIT = 1, int HS = 1>
 __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
     constexpr int KG = BC / 32;           // 32-key units per block
     constexpr int UPP = W * UW;           // units per phase
@@ -78,6 +84,7 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
     constexpr int FRV = DV / 16;          // 16-byte fragments per lane per V unit
     constexpr int CPRV = DV / 8;          // 16-byte chunks per staged V row
     static_assert(DSPLIT == 1 || DSPLIT == 2, "one or two workgroups per split");
+    static_assert(HS == 1 || (DSPLIT == 1 && !MARGINS), "head parts: full-width V pass, no margin pass");
     static_assert(UPP % KG == 0, "units must tile the phase");
     static_assert(BPP <= 32, "decision masks are 32-bit");
     static_assert(W * DTV * 4 * 64 * 4 <= NSLOT * W * VSLOT, "O reduction must fit the staging area");
@@ -98,13 +105,15 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
     __shared__ float lds_pmax[2][UPP * HT];
     __shared__ float lds_l[W][64];
 
-    int split = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z, half = 0;
-    if constexpr (DSPLIT == 2) {
-        // 1-D grid: workgroups L and L + 8 form a pair (same unit, halves 0 and 1),
-        // so that both land on the same XCD (workgroups go round-robin over 8)
+    int split = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z, half = 0, part = 0;
+    if constexpr (DSPLIT * HS > 1) {
+        // 1-D grid: workgroups L, L + 8, ... form a unit's DSPLIT * HS parts, so
+        // that they land on the same XCD (workgroups go round-robin over 8)
+        constexpr int NP = DSPLIT * HS;
         const int L = blockIdx.x;
-        const int unit = (L / 16) * 8 + (L % 8);
-        half = (L / 8) & 1;
+        const int unit = (L / (8 * NP)) * 8 + (L % 8);
+        part = (L / 8) % NP;
+        half = DSPLIT == 2 ? part : 0;
         if (unit >= a.S * a.Hkv * a.B) return;
         split = unit % a.S;
         hkv = (unit / a.S) % a.Hkv;
@@ -117,6 +126,7 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
     // partition the sequence's own blocks; a split left without one (S > nk)
     // writes the merge identity, O = 0 and LSE = -inf.
     const int G = a.G;
+    const int h0 = HS > 1 ? part * HT : 0;  // this workgroup's first head of the group
     const int N = a.lens ? __builtin_amdgcn_readfirstlane(min(max(a.lens[b], 0), a.N)) : a.N;
     const int nk = a.lens ? (N + BC - 1) / BC : a.nk;
     const int j0 = (int)((int64_t)split * nk / a.S);
@@ -124,7 +134,7 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
 
     const uint16_t* kbase = a.k + ((size_t)b * a.Hkv + hkv) * (size_t)a.N * D;
     const uint16_t* vbase = a.v + ((size_t)b * a.Hkv + hkv) * (size_t)a.N * D;
-    if (a.lens && split == a.S - 1 && nk < a.nk && half == 0) {
+    if (a.lens && split == a.S - 1 && nk < a.nk && part == 0) {
         // blocks past the sequence's end are not visited (2)
         for (int x = threadIdx.x; x < (G + 1) * (a.nk - nk); x += 64 * W) {
             const int r = x / (a.nk - nk), j = nk + x % (a.nk - nk);
@@ -139,7 +149,7 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
     bool head_ok[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-        const int h = nt * 16 + n;
+        const int h = h0 + nt * 16 + n;
         head_ok[nt] = h < G;
         const uint16_t* qrow = a.q + ((size_t)b * a.Hq + (size_t)hkv * G + (head_ok[nt] ? h : 0)) * D;
 #pragma unroll
@@ -356,7 +366,7 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
         if (a.skip != nullptr && half == 0) {
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
-                const int h = nt * 16 + n;
+                const int h = h0 + nt * 16 + n;
                 if (!head_ok[nt]) continue;
                 uint8_t* row = a.skip + ((size_t)b * a.Hq + (size_t)hkv * G + h) * a.nk + p0;
                 for (int bi = wave * 4 + g; bi < nb; bi += 4 * W) row[bi] = (uint8_t)(((keep[nt] >> bi) & 1u) ^ 1u);
@@ -364,7 +374,11 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
         }
         if (a.vskip != nullptr && half == 0) {
             uint8_t* row = a.vskip + ((size_t)b * a.Hkv + hkv) * a.nk + p0;
-            for (int bi = threadIdx.x; bi < nb; bi += 64 * W) row[bi] = (uint8_t)(((vkeep >> bi) & 1u) ^ 1u);
+            for (int bi = threadIdx.x; bi < nb; bi += 64 * W) {
+                const uint8_t skipped = (uint8_t)(((vkeep >> bi) & 1u) ^ 1u);
+                if (HS == 1) row[bi] = skipped;
+                else if (!skipped) row[bi] = 0;  // parts that load the block all store the same 0
+            }
         }
 
         // ================= V pass (kept units only) =================
@@ -453,7 +467,7 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
         float lt = 0.f;
 #pragma unroll
         for (int w = 0; w < W; ++w) lt += lds_l[w][lane];
-        const int h = nt * 16 + n;
+        const int h = h0 + nt * 16 + n;
         if (h < G) {
             const size_t orow = ((size_t)b * a.Hq + (size_t)hkv * G + h) * a.S + split;
             const float inv = lt > 0.f ? 1.f / lt : 0.f;  // 0: a split with no block
@@ -537,11 +551,34 @@ hipError_t launch_split_pairs(const DecodeArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// Sets n bytes to v.
+__global__ __launch_bounds__(256) void fill_u8_kernel(uint8_t* __restrict__ p, size_t n, uint8_t v) {
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+// HS workgroups per split, each HT = 16 NT heads of the group, 8 apart in a 1-D
+// grid.  The V skip mask starts as all "not loaded"; the parts clear the bytes
+// of the blocks they load.
+template <int D, int BC, int NT, int UW, int W, int NSLOT, int HS>
+hipError_t launch_split_heads(const DecodeArgs& a, hipStream_t stream) {
+    if (a.vskip != nullptr) {
+        const size_t n = (size_t)a.B * a.Hkv * a.nk;
+        hipLaunchKernelGGL(fill_u8_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a.vskip, n,
+                           (uint8_t)1);
+    }
+    const int64_t units = (int64_t)a.S * a.Hkv * a.B;
+    if (HS * ((units + 7) / 8) * 8 > INT_MAX) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)(HS * ((units + 7) / 8) * 8));
+    hipLaunchKernelGGL((decode_split_kernel<D, BC, NT, UW, W, NSLOT, false, 1, HS>), grid, dim3(64 * W), 0, stream, a);
+    return hipGetLastError();
+}
+
 // The margin pass reads K only; the four-wave shape keeps 128 KiB in flight.
 template <int D, int BC>
 hipError_t launch_margins_nt(const DecodeArgs& a, hipStream_t stream) {
     if (a.G <= 16) return launch_split<D, BC, 1, 16, 4, 4, true>(a, stream);
-    if (a.G <= 32) return launch_split<D, BC, 2, 4, 8, 2, true>(a, stream);
+    if (a.G <= 32) return launch_split<D, BC, 2, 8, 4, 4, true>(a, stream);
     return launch_split<D, BC, 4, 2, 4, 2, true>(a, stream);
 }
 
@@ -556,8 +593,9 @@ hipError_t launch_split_nt(const DecodeArgs& a, hipStream_t stream) {
         if ((int64_t)a.S * a.Hkv * a.B <= 256) return launch_split<D, BC, 1, 8, 8, 2>(a, stream);
         return launch_split<D, BC, 1, 16, 4, 4>(a, stream);
     }
-    if (a.G <= 32) return launch_split<D, BC, 2, 4, 8, 2>(a, stream);
-    return launch_split<D, BC, 4, 2, 4, 2>(a, stream);
+    if (a.G <= 32) return launch_split<D, BC, 2, 8, 4, 4>(a, stream);
+    if (a.G <= 64) return launch_split<D, BC, 4, 2, 4, 2>(a, stream);
+    return launch_split_heads<D, BC, 4, 2, 4, 2, 2>(a, stream);
 }
 
 }  // namespace

@@ -101,7 +101,7 @@ blasst_status blasst_prefill(const void* q, const void* k, const void* v, float*
  *   num_splits 1 <= num_splits <= ceil(N/Bc)
  * Errors: INVALID_ARG for a null q/k/v/o_part/lse_part, B/Hq < 0, N <= 0,
  * gqa_ratio < 1 or not dividing Hq, lambda outside [0,1), bad num_splits;
- * UNSUPPORTED for d or Bc outside {64, 128}, or gqa_ratio > 64.  Scalar
+ * UNSUPPORTED for d or Bc outside {64, 128}, or gqa_ratio > 128.  Scalar
  * arguments are checked first; then B*Hq == 0 returns OK and does nothing (the
  * pointers may then be NULL and are not read).
  */
@@ -244,8 +244,8 @@ blasst_status blasst_prefill_margins(const void* q, const void* k, float* margin
  *            max restarting at each of the num_splits splits.
  *   vmargin  fp32 [B, Hkv, ceil(N/Bc)] or NULL: the max of D over the kv
  *            group's heads (the V block is not loaded iff it is < ln(lambda)).
- * Errors and argument rules as blasst_decode (lambda absent); a null margin is
- * INVALID_ARG.
+ * Errors and argument rules as blasst_decode (lambda absent), except that
+ * gqa_ratio > 64 is UNSUPPORTED; a null margin is INVALID_ARG.
  */
 blasst_status blasst_decode_margins(const void* q, const void* k, float* margin, float* vmargin, int B, int Hq,
                                     int N, int d, int gqa_ratio, int Bc, int num_splits, blasst_stream_t stream);

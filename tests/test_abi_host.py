@@ -78,7 +78,7 @@ def test_prefill_validation(lib, kw, status):
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), 1), (dict(N=0), 1), (dict(S=0), 1), (dict(S=3), 1), (dict(G=5), 1),
     (dict(lam=1.5), 1), (dict(causal=-1), 1), (dict(d=80), 2), (dict(Bc=256, S=1), 2),
-    (dict(Hq=128, G=128), 2), (dict(B=0), 0), (dict(Hq=0), 0),
+    (dict(Hq=256, G=256), 2), (dict(B=0), 0), (dict(Hq=0), 0),
 ])
 def test_decode_validation(lib, kw, status):
     assert decode(lib, **kw) == status
@@ -143,7 +143,7 @@ def test_prefill_ragged_validation(lib, kw, status):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(lens=None), 1), (dict(lens=P(0x1001)), 1), (dict(q=None), 1), (dict(N=0), 1), (dict(S=3), 1),
-    (dict(S=0), 1), (dict(lam=-1.0), 1), (dict(Bc=256, S=1), 2), (dict(Hq=128, G=128), 2),
+    (dict(S=0), 1), (dict(lam=-1.0), 1), (dict(Bc=256, S=1), 2), (dict(Hq=256, G=256), 2),
     (dict(B=0, lens=None), 0),
 ])
 def test_decode_ragged_validation(lib, kw, status):

@@ -40,6 +40,9 @@ DECODE_SMALL = [
     (1, 2, 2, 777, 128, 128, 2, 0.05, 0),      # MHA, ragged
     (1, 8, 2, 40960, 128, 128, 8, 0.01, 256),  # paired workgroups, 40 blocks per split: phases of 16, 16, 8
     (1, 4, 1, 9000, 64, 64, 2, 0.02, 128),     # paired, d = Bc = 64, 71 blocks per split: phases of 32, 32, 7
+    (2, 40, 2, 2500, 128, 64, 3, 0.02, 0),     # G = 20: a partly filled 32-head tile
+    (1, 128, 1, 3000, 128, 128, 4, 0.02, 128), # G = 128: two 64-head workgroups per split, ragged
+    (2, 96, 1, 2100, 64, 64, 3, 0.02, 0),      # G = 96: the second 64-head part half filled
 ]
 
 

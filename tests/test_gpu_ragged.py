@@ -113,6 +113,7 @@ DECODE = [
     (2, 64, 1, 2000, 128, 128, 3, 0, [1, 2000]),               # MQA, a single key
     (4, 16, 1, 1536, 128, 64, 8, 0, [1536, 700, 300, 1]),
     (2, 8, 2, 40960, 128, 128, 8, 256, [40960, 23000]),      # paired workgroups, several phases per split
+    (3, 128, 1, 1500, 128, 128, 4, 0, [1500, 0, 333]),         # G = 128: two head parts per split
 ]
 
 
