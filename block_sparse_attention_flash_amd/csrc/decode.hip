@@ -20,8 +20,10 @@
 //           MFMA A layout (ds_read_b128).  S^T = K q^T runs on MFMA 16x16x32
 //           bf16 with the 32 keys as two 16-row tiles and the G query heads of
 //           the group as 16-wide column tiles (heads beyond G are zero columns
-//           that never vote).  The S^T tiles stay in registers; each unit's
-//           per-head partial max goes to LDS.
+//           that never vote).  q^T sits in registers, or for four head tiles
+//           in LDS, read per unit (its registers then hold S^T tiles).  The
+//           S^T tiles stay in registers; each unit's per-head partial max goes
+//           to LDS.
 //  decide   a barrier; every lane then walks the phase's blocks in order.
 //           Because a skipped block never moves the running max
 //           (mt < m + ln(lambda) < m), the running max before block j is the
@@ -104,6 +106,9 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) char lds_v[NSLOT * W * VSLOT];
     __shared__ float lds_pmax[2][UPP * HT];
     __shared__ float lds_l[W][64];
+    // Four head tiles: q^T is read from LDS per unit (its registers hold S^T tiles instead)
+    constexpr bool QL = NT >= 4;
+    __shared__ __attribute__((aligned(16))) char lds_q[QL ? HT * D * 2 : 16];
 
     int split = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z, half = 0, part = 0;
     if constexpr (DSPLIT * HS > 1) {
@@ -145,19 +150,34 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
     }
 
     // q^T as the B operand: lane (g, n) holds q[head n][32s + 8g .. +8].
-    bf16x8 qf[NT][DS];
+    bf16x8 qf[QL ? 1 : NT][DS];
     bool head_ok[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         const int h = h0 + nt * 16 + n;
         head_ok[nt] = h < G;
-        const uint16_t* qrow = a.q + ((size_t)b * a.Hq + (size_t)hkv * G + (head_ok[nt] ? h : 0)) * D;
+        if constexpr (!QL) {
+            const uint16_t* qrow = a.q + ((size_t)b * a.Hq + (size_t)hkv * G + (head_ok[nt] ? h : 0)) * D;
 #pragma unroll
-        for (int s = 0; s < DS; ++s) {
-            u32x4 z = {0u, 0u, 0u, 0u};
-            qf[nt][s] = as_bf16x8(head_ok[nt] ? load16(qrow + 32 * s + 8 * g) : z);
+            for (int s = 0; s < DS; ++s) {
+                u32x4 z = {0u, 0u, 0u, 0u};
+                qf[nt][s] = as_bf16x8(head_ok[nt] ? load16(qrow + 32 * s + 8 * g) : z);
+            }
         }
     }
+    // QL: the group's q rows (zero beyond G), chunk c of row r at chunk c ^ (r mod CPR)
+    constexpr int QCH = QL ? HT * CPR / (64 * W) : 1;  // 16-byte chunks per thread
+    static_assert(!QL || HT * CPR % (64 * W) == 0, "q chunks must split evenly over the threads");
+    u32x4 qst[QCH];
+    if constexpr (QL) {
+#pragma unroll
+        for (int x = 0; x < QCH; ++x) {
+            const int e = x * 64 * W + threadIdx.x, r = e / CPR, c = e % CPR;
+            const int h = h0 + r;
+            qst[x] = h < G ? load16(a.q + ((size_t)b * a.Hq + (size_t)hkv * G + h) * D + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    bool q_staged = !QL;
 
     f32x4 oacc[NT][DTV];
     float m_run[NT], l_part[NT];
@@ -203,6 +223,17 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
         };
 #pragma unroll
         for (int u = 0; u < (NSLOT < UW ? NSLOT : UW); ++u) issue_k(u);
+        if constexpr (QL) {
+            if (!q_staged) {  // first phase: q goes to LDS while the first K copies are in flight
+#pragma unroll
+                for (int x = 0; x < QCH; ++x) {
+                    const int e = x * 64 * W + threadIdx.x, r = e / CPR, c = e % CPR;
+                    *(u32x4*)(lds_q + r * (2 * D) + ((c ^ (r & (CPR - 1))) << 4)) = qst[x];
+                }
+                __syncthreads();
+                q_staged = true;
+            }
+        }
 
         // ---- decisions (prefix max of the block maxima; no cascade): blocks
         //      [lo, hi) of the phase, continuing the running max m_dec
@@ -313,11 +344,21 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
                 float pm = kNegInf;
+                bf16x8 qv[DS];
+#pragma unroll
+                for (int s = 0; s < DS; ++s) {
+                    if constexpr (QL) {
+                        const int r = nt * 16 + n, c = 4 * s + g;
+                        qv[s] = as_bf16x8(*(const u32x4*)(lds_q + r * (2 * D) + ((c ^ (r & (CPR - 1))) << 4)));
+                    } else {
+                        qv[s] = qf[nt][s];
+                    }
+                }
 #pragma unroll
                 for (int kt = 0; kt < 2; ++kt) {
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int s = 0; s < DS; ++s) acc = mfma16x16x32(as_bf16x8(kf[kt][s]), qf[nt][s], acc);
+                    for (int s = 0; s < DS; ++s) acc = mfma16x16x32(as_bf16x8(kf[kt][s]), qv[s], acc);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int key = ukey0[u] + 16 * kt + 4 * g + i;
