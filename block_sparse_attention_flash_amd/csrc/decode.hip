@@ -635,7 +635,12 @@ hipError_t launch_split_nt(const DecodeArgs& a, hipStream_t stream) {
         return launch_split<D, BC, 1, 16, 4, 4>(a, stream);
     }
     if (a.G <= 32) return launch_split<D, BC, 2, 8, 4, 4>(a, stream);
-    if (a.G <= 64) return launch_split<D, BC, 4, 2, 4, 2>(a, stream);
+    if (a.G <= 64) {
+        // few units: pairs, each with four slots per wave (46 -> 37 us at 2 x 64 heads x 32K, 16 splits);
+        // many: one workgroup per unit (128 vs 173 us for pairs at 64 x 64 heads x 16K, 8 splits)
+        if ((int64_t)a.S * a.Hkv * a.B <= 128) return launch_split_pairs<D, BC, 4, 4, 4, 4>(a, stream);
+        return launch_split<D, BC, 4, 2, 4, 2>(a, stream);
+    }
     return launch_split_heads<D, BC, 4, 2, 4, 2, 2>(a, stream);
 }
 

@@ -36,7 +36,8 @@ DECODE_SMALL = [
     (2, 8, 2, 2048, 128, 128, 4, 0.01, 128),
     (1, 16, 1, 1536, 128, 64, 24, 0.02, 0),    # one block per split
     (1, 32, 1, 4096, 128, 128, 1, 0.02, 0),    # G = 32, a single split
-    (2, 64, 1, 3000, 64, 128, 5, 0.02, 0),     # MQA, G = 64, ragged
+    (2, 64, 1, 3000, 64, 128, 5, 0.02, 0),     # MQA, G = 64, ragged (paired workgroups)
+    (33, 64, 1, 600, 64, 64, 4, 0.02, 0),      # MQA, 132 units: one workgroup per unit
     (1, 2, 2, 777, 128, 128, 2, 0.05, 0),      # MHA, ragged
     (1, 8, 2, 40960, 128, 128, 8, 0.01, 256),  # paired workgroups, 40 blocks per split: phases of 16, 16, 8
     (1, 4, 1, 9000, 64, 64, 2, 0.02, 128),     # paired, d = Bc = 64, 71 blocks per split: phases of 32, 32, 7
