@@ -82,7 +82,8 @@ def parse():
     p.add_argument("--no-mla", action="store_true")
     p.add_argument("--all-configs", action="store_true",
                    help="also time every workload configuration (prefill_1k_tiny, decode_128k_b16, decode_mqa_16k "
-                        "besides the two 32K ones): time, fraction of the roofline, block sparsity")
+                        "besides the two 32K ones) and two ragged batches: time, fraction of the roofline, "
+                        "block sparsity")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--profile-target", choices=["decode", "prefill", "copy"], default=None,
@@ -454,6 +455,102 @@ def bench_config(name, args, lib, torch, W):
                 block_sparsity=round(float(sk.mean()), 5), vload_sparsity=round(float(vsk.mean()), 5))
 
 
+def bench_ragged(args, lib, torch, W):
+    """Ragged batches through blasst_decode_ragged / blasst_prefill_ragged: a decode serving batch of 16
+    sequences with 1K-32K contexts in a 32K-capacity cache (the GPU test's recipe), and a causal prefill
+    of four sequences of 16K, 9K, 4K and 1.5K rows in a 16K-capacity buffer.  Work is counted over each
+    sequence's own length: the K rows and kept V rows of its context (decode), the visited and kept tiles
+    of its causal range (prefill)."""
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    f32 = dict(dtype=torch.float32, device="cuda")
+
+    def ok(st):
+        if st != 0:
+            raise RuntimeError("libblasst call failed with status %d" % st)
+
+    def trials(fn, reps):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(TRIALS):
+            s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s0.record(stream)
+            for _ in range(reps):
+                fn()
+            s1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(s0.elapsed_time(s1) / reps)
+        return float(np.median(ts)), min(ts), max(ts)
+
+    # ---- decode serving batch
+    rng = np.random.default_rng(7)
+    lens = [int(v) for v in rng.integers(1024, 32769, size=16)]
+    lens[3] = 32768
+    w = W.Workload("decode_ragged_serving", "decode", B=16, Hq=32, Hkv=8, d=128, T=32768, Bc=128,
+                   lambdas=(1e-3,), hot_rate=0.01, seed=707, window=512, num_splits=16)
+    B, Hq, Hkv, N, d, Bc, S, lam = w.B, w.Hq, w.Hkv, w.T, w.d, w.Bc, w.num_splits, w.lambdas[0]
+    nk = -(-N // Bc)
+    xd = {k: dev(v) for k, v in W.generate(w).items()}
+    lens_d = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    o_part = torch.empty((B, Hq, S, d), **f32)
+    lse_part = torch.empty((B, Hq, S), **f32)
+    o = torch.empty((B, Hq, d), **f32)
+    lse = torch.empty((B, Hq), **f32)
+    skip = torch.empty((B, Hq, nk), dtype=torch.uint8, device="cuda")
+    vskip = torch.empty((B, Hkv, nk), dtype=torch.uint8, device="cuda")
+    sa = (P(xd["q"]), P(xd["k"]), P(xd["v"]), P(o_part), P(lse_part), P(skip), P(vskip), P(lens_d), B, Hq, N, d,
+          Hq // Hkv, Bc, ctypes.c_double(lam), S, sp)
+    ca = (P(o_part), P(lse_part), P(o), P(lse), B, Hq, d, S, sp)
+    split_ms, lo, hi = trials(lambda: ok(lib.blasst_decode_ragged(*sa)), 50)
+    step_ms, _, _ = trials(lambda: (ok(lib.blasst_decode_ragged(*sa)), ok(lib.blasst_decode_combine(*ca))), 50)
+    vsk = vskip.cpu().numpy()
+    kept_rows = 0
+    for b, L in enumerate(lens):
+        rows = np.minimum(Bc, L - np.arange(-(-L // Bc)) * Bc)
+        kept_rows += int(((vsk[b, :, :len(rows)] == 0) * rows[None, :]).sum())
+    split_bytes = (Hkv * sum(lens) * d * 2 + kept_rows * d * 2 + B * Hq * d * 2 + B * Hq * S * (d + 1) * 4
+                   + (B * Hq + B * Hkv) * nk)
+    comb_bytes = B * Hq * S * (d + 1) * 4 + B * Hq * (d + 1) * 4
+    gbs = split_bytes / (split_ms * 1e-3) / 1e9
+    dec = dict(lens=lens, capacity=N, B=B, Hq=Hq, Hkv=Hkv, d=d, Bc=Bc, num_splits=S, lam=lam,
+               split_kernel_us=round(split_ms * 1e3, 2), split_kernel_us_min=round(lo * 1e3, 2),
+               split_kernel_us_max=round(hi * 1e3, 2), step_us=round(step_ms * 1e3, 2),
+               bytes_per_split_launch=split_bytes, split_GBs=round(gbs, 1),
+               frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4),
+               step_GBs=round((split_bytes + comb_bytes) / (step_ms * 1e-3) / 1e9, 1),
+               vload_sparsity=round(1.0 - kept_rows / (Hkv * sum(lens)), 5))
+    del xd
+    torch.cuda.empty_cache()
+
+    # ---- causal prefill, four sequences
+    plens = [16384, 9000, 4000, 1500]
+    w = W.Workload("prefill_ragged", "prefill", B=4, Hq=32, Hkv=8, d=128, T=16384, Bc=128, lambdas=(1e-3,),
+                   hot_rate=0.01, seed=708)
+    B, Hq, T, d, Bc, lam = w.B, w.Hq, w.T, w.d, w.Bc, w.lambdas[0]
+    nq = -(-T // Bc)
+    xd = {k: dev(v) for k, v in W.generate(w).items()}
+    lens_d = torch.tensor(plens, dtype=torch.int32, device="cuda")
+    o = torch.empty((B, Hq, T, d), **f32)
+    lse = torch.empty((B, Hq, T), **f32)
+    mask = torch.empty((B, Hq, nq, nq), dtype=torch.uint8, device="cuda")
+    pa = (P(xd["q"]), P(xd["k"]), P(xd["v"]), P(o), P(lse), P(mask), P(lens_d), B, Hq, T, d, Hq // w.Hkv, Bc,
+          ctypes.c_double(lam), 1, sp)
+    ms, lo, hi = trials(lambda: ok(lib.blasst_prefill_ragged(*pa)), 5)
+    m = mask.cpu().numpy()
+    visited, skipped = int((m != 2).sum()), int((m == 1).sum())
+    flops = (2 * visited - skipped) * 2.0 * Bc * Bc * d
+    tf = flops / (ms * 1e-3) / 1e12
+    pre = dict(lens=plens, capacity=T, B=B, Hq=Hq, Hkv=w.Hkv, d=d, Bc=Bc, lam=lam, ms=round(ms, 4),
+               ms_min=round(lo, 4), ms_max=round(hi, 4), tflops_executed=round(tf, 2),
+               frac_of_mfma_peak=round(tf / MFMA_BF16_PEAK_TFLOPS, 4), block_sparsity=round(skipped / visited, 5))
+    del xd
+    torch.cuda.empty_cache()
+    return {"decode_serving_batch": dec, "prefill_causal": pre}
+
+
 def bench_mla(args, lib, torch, W):
     """MLA decode split kernel at 32K context, with 64- and 32-token blocks: time, HBM bytes (the cache
     rows are read once), the executed FLOPs (S for every head and token; P V for the kept blocks of each
@@ -588,6 +685,7 @@ def main():
         for name in ("prefill_1k_tiny", "decode_128k_b16", "decode_mqa_16k"):
             configs[name] = bench_config(name, args, lib, torch, W)
             torch.cuda.empty_cache()
+        configs["ragged"] = bench_ragged(args, lib, torch, W)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args, d)
 
     by = d["bytes"]
