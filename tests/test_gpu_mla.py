@@ -60,7 +60,7 @@ MLA32 = [
 
 @pytest.mark.parametrize("shape,Bc", [(s, 64) for s in MLA] + [(s, 32) for s in MLA32],
                          ids=lambda v: ("B%d_Hq%d_N%d_S%d" % v) if isinstance(v, tuple) else "Bc%d" % v)
-@pytest.mark.parametrize("lam", [0.0, 1e-3, 1e-1])
+@pytest.mark.parametrize("lam", [0.0, 1e-3, 1e-1, 0.99])
 def test_mla_small(shape, Bc, lam):
     B, Hq, N, S = shape
     q, kv = mla_inputs(B, Hq, N, S, seed=900 + N, Bc=Bc)

@@ -48,7 +48,7 @@ DECODE_SMALL = [
 
 
 @pytest.mark.parametrize("shape", DECODE_SMALL, ids=lambda s: "B%d_Hq%d_Hkv%d_N%d_d%d_Bc%d_S%d" % s[:7])
-@pytest.mark.parametrize("lam", [0.0, 1e-3, 1e-1])
+@pytest.mark.parametrize("lam", [0.0, 1e-3, 1e-1, 0.99])
 def test_decode_small(shape, lam):
     B, Hq, Hkv, N, d, Bc, S, hot, window = shape
     w = W.Workload("t", "decode", B=B, Hq=Hq, Hkv=Hkv, d=d, T=N, Bc=Bc, lambdas=(lam,), hot_rate=hot,
@@ -69,7 +69,7 @@ PREFILL_SMALL = [
 
 
 @pytest.mark.parametrize("shape", PREFILL_SMALL, ids=lambda s: "B%d_Hq%d_Hkv%d_T%d_d%d_Bc%d" % s[:6])
-@pytest.mark.parametrize("lam", [0.0, 1e-4, 1e-2, 0.5])
+@pytest.mark.parametrize("lam", [0.0, 1e-4, 1e-2, 0.5, 0.99])
 @pytest.mark.parametrize("causal", [True, False])
 def test_prefill_small(shape, lam, causal):
     B, Hq, Hkv, T, d, Bc, hot = shape
