@@ -576,6 +576,55 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restri
     if (e == 0 && lse != nullptr) lse[row] = total;
 }
 
+// The same merge with four columns per thread (16-byte loads and stores) and
+// 256 / (D / 4) rows per workgroup, for 16-byte aligned partials and outputs.
+template <int D>
+__global__ __launch_bounds__(256) void decode_combine4_kernel(const float* __restrict__ o_part,
+                                                              const float* __restrict__ lse_part,
+                                                              float* __restrict__ o, float* __restrict__ lse,
+                                                              int S, int rows) {
+    constexpr int TPR = D / 4;          // threads per row
+    constexpr int RPW = 256 / TPR;      // rows per workgroup
+    constexpr int SMAX = 32;
+    const int r = blockIdx.x * RPW + (int)threadIdx.x / TPR;
+    if (r >= rows) return;
+    const size_t row = (size_t)r;
+    const int e = threadIdx.x % TPR;
+    const float* L = lse_part + row * S;
+    const f32x4* op = (const f32x4*)(o_part + row * S * D) + e;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float top = kNegInf, total;
+    if (S <= SMAX) {
+        float lv[SMAX];
+        f32x4 xv[SMAX];
+#pragma unroll
+        for (int s = 0; s < SMAX; ++s) {
+            lv[s] = s < S ? L[s] : kNegInf;
+            xv[s] = s < S ? op[(size_t)s * TPR] : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int s = 0; s < SMAX; ++s) top = fmaxf(top, lv[s]);
+        // every split empty (no key at all): O = 0, LSE = -inf
+        const float ref = top == kNegInf ? 0.f : top;
+        float z = 0.f;
+#pragma unroll
+        for (int s = 0; s < SMAX; ++s) z += exp2_fast((lv[s] - ref) * kLog2e);
+        total = ref + logf(z);
+#pragma unroll
+        for (int s = 0; s < SMAX; ++s) acc += exp2_fast((lv[s] - total) * kLog2e) * xv[s];
+    } else {
+        for (int s = 0; s < S; ++s) top = fmaxf(top, L[s]);
+        const float ref = top == kNegInf ? 0.f : top;
+        float z = 0.f;
+        for (int s = 0; s < S; ++s) z += exp2_fast((L[s] - ref) * kLog2e);
+        total = ref + logf(z);
+        for (int s = 0; s < S; ++s) acc += exp2_fast((L[s] - total) * kLog2e) * op[(size_t)s * TPR];
+    }
+    if (top == kNegInf) acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    *((f32x4*)(o + row * D) + e) = acc;
+    if (e == 0 && lse != nullptr) lse[row] = total;
+}
+
 template <int D, int BC, int NT, int UW, int W, int NSLOT, bool MARGINS = false>
 hipError_t launch_split(const DecodeArgs& a, hipStream_t stream) {
     dim3 grid(a.S, a.Hkv, a.B);
@@ -658,6 +707,18 @@ hipError_t launch_decode_margins(const DecodeArgs& a, int d, int Bc, hipStream_t
 
 hipError_t launch_decode_combine(const float* o_part, const float* lse_part, float* o, float* lse, int rows,
                                  int d, int S, hipStream_t stream) {
+    if ((((uintptr_t)o_part | (uintptr_t)o) & 15u) == 0) {
+        // 16-byte aligned: four columns per thread, several rows per workgroup
+        const int rpw = 256 / (d / 4);
+        const dim3 grid((unsigned)((rows + rpw - 1) / rpw));
+        if (d == 512)
+            hipLaunchKernelGGL(decode_combine4_kernel<512>, grid, dim3(256), 0, stream, o_part, lse_part, o, lse, S, rows);
+        else if (d == 128)
+            hipLaunchKernelGGL(decode_combine4_kernel<128>, grid, dim3(256), 0, stream, o_part, lse_part, o, lse, S, rows);
+        else
+            hipLaunchKernelGGL(decode_combine4_kernel<64>, grid, dim3(256), 0, stream, o_part, lse_part, o, lse, S, rows);
+        return hipGetLastError();
+    }
     if (d == 512)
         hipLaunchKernelGGL(decode_combine_kernel<512>, dim3(rows), dim3(512), 0, stream, o_part, lse_part, o, lse, S);
     else if (d == 128)

@@ -193,3 +193,32 @@ def test_argument_errors():
     with pytest.raises(bsa.BlasstError) as e:
         bsa.prefill(q96, q96, q96, 1e-3, Bc=64)
     assert e.value.status == bsa.ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("d,S", [(128, 16), (64, 40), (512, 5)])
+def test_combine_paths_agree(d, S):
+    """The merge runs four columns per thread when the partials and the output are 16-byte
+    aligned, one column per thread otherwise; both give bit-identical results, including a row
+    whose splits are all empty and one with a single non-empty split (S = 40: the looped form)."""
+    import torch
+    import block_sparse_attention_flash_amd as bsa
+    g = torch.Generator().manual_seed(d + S)
+    B, Hq = 3, 5
+    o_part = torch.randn((B, Hq, S, d), generator=g).cuda()
+    lse_part = (torch.randn((B, Hq, S), generator=g) * 3).cuda()
+    lse_part[0, 0, :] = float("-inf")
+    lse_part[1, 2, 1:] = float("-inf")
+    o_a, l_a = bsa.decode_combine(o_part, lse_part)
+
+    def shifted(t):  # same values, 4 bytes past a 16-byte boundary
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+        v = buf[1:].view(t.shape)
+        v.copy_(t)
+        return v
+
+    op_u, o_u, l_u = shifted(o_part), shifted(torch.zeros_like(o_a)), torch.empty_like(l_a)
+    bsa.blasst_decode_combine(op_u, lse_part, o_u, l_u)
+    torch.cuda.synchronize()
+    assert torch.equal(o_a, o_u) and torch.equal(l_a, l_u)
+    assert torch.all(o_a[0, 0] == 0) and l_a[0, 0] == float("-inf")
+    assert torch.allclose(o_a[1, 2], o_part[1, 2, 0]) and l_a[1, 2] == lse_part[1, 2, 0]
