@@ -224,7 +224,7 @@ BLASST_EXPORT blasst_status blasst_decode_margins(const void* q, const void* k, 
         const int64_t nk = ((int64_t)N + Bc - 1) / Bc;
         if (num_splits < 1 || num_splits > nk) return BLASST_ERR_INVALID_ARG;
         if (!supported_dim(d) || !supported_dim(Bc)) return BLASST_ERR_UNSUPPORTED;
-        if (gqa_ratio > 64) return BLASST_ERR_UNSUPPORTED;
+        if (gqa_ratio > 128) return BLASST_ERR_UNSUPPORTED;  // at most two 64-head workgroups per split
         if ((int64_t)B * Hq == 0) return BLASST_OK;  // nothing to do; pointers are not read
         if (!q || !k || !margin) return BLASST_ERR_INVALID_ARG;
         if (!aligned16(q) || !aligned16(k)) return BLASST_ERR_INVALID_ARG;

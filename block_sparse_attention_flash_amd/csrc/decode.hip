@@ -86,7 +86,7 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
     constexpr int FRV = DV / 16;          // 16-byte fragments per lane per V unit
     constexpr int CPRV = DV / 8;          // 16-byte chunks per staged V row
     static_assert(DSPLIT == 1 || DSPLIT == 2, "one or two workgroups per split");
-    static_assert(HS == 1 || (DSPLIT == 1 && !MARGINS), "head parts: full-width V pass, no margin pass");
+    static_assert(HS == 1 || DSPLIT == 1, "head parts run the full-width V pass");
     static_assert(UPP % KG == 0, "units must tile the phase");
     static_assert(BPP <= 32, "decision masks are 32-bit");
     static_assert(W * DTV * 4 * 64 * 4 <= NSLOT * W * VSLOT, "O reduction must fit the staging area");
@@ -274,8 +274,8 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
                             if constexpr (MARGINS) {
                                 const float dm = head_ok[nt] ? (bm - m) * kLn2 : kNegInf;
                                 if (wave == 0 && g == 0 && head_ok[nt])
-                                    a.margin[((size_t)b * a.Hq + (size_t)hkv * G + nt * 16 + n) * a.nk + p0 + bi] = dm;
-                                if (a.vmargin != nullptr) vmax_blk[bi] = fmaxf(vmax_blk[bi], row16_max(dm));
+                                    a.margin[((size_t)b * a.Hq + (size_t)hkv * G + h0 + nt * 16 + n) * a.nk + p0 + bi] = dm;
+                                if (HS == 1 && a.vmargin != nullptr) vmax_blk[bi] = fmaxf(vmax_blk[bi], row16_max(dm));
                             }
                         }
                     }
@@ -395,7 +395,8 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
         }
         vkeep = row16_or(vkeep);
         if constexpr (MARGINS) {
-            if (a.vmargin != nullptr && wave == 0 && lane == 0) {
+            // (head parts: the launcher forms the group's max from the per-head margins)
+            if (HS == 1 && a.vmargin != nullptr && wave == 0 && lane == 0) {
                 float* vrow = a.vmargin + ((size_t)b * a.Hkv + hkv) * a.nk + p0;
                 for (int bi = 0; bi < nb; ++bi) vrow[bi] = vmax_blk[bi];
             }
@@ -650,9 +651,22 @@ __global__ __launch_bounds__(256) void fill_u8_kernel(uint8_t* __restrict__ p, s
 // HS workgroups per split, each HT = 16 NT heads of the group, 8 apart in a 1-D
 // grid.  The V skip mask starts as all "not loaded"; the parts clear the bytes
 // of the blocks they load.
-template <int D, int BC, int NT, int UW, int W, int NSLOT, int HS>
+// The margin pass with head parts: each group's max of D over its heads, per
+// block, from the per-head margins the parts wrote (rows (b, hkv) * G + h).
+__global__ __launch_bounds__(256) void group_margin_kernel(const float* __restrict__ margin,
+                                                           float* __restrict__ vmargin, int G, int nk, size_t n) {
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const size_t bh = i / nk, j = i % nk;
+    const float* m = margin + bh * G * nk + j;
+    float v = kNegInf;
+    for (int h = 0; h < G; ++h) v = fmaxf(v, m[(size_t)h * nk]);
+    vmargin[i] = v;
+}
+
+template <int D, int BC, int NT, int UW, int W, int NSLOT, int HS, bool MARGINS = false>
 hipError_t launch_split_heads(const DecodeArgs& a, hipStream_t stream) {
-    if (a.vskip != nullptr) {
+    if (!MARGINS && a.vskip != nullptr) {
         const size_t n = (size_t)a.B * a.Hkv * a.nk;
         hipLaunchKernelGGL(fill_u8_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a.vskip, n,
                            (uint8_t)1);
@@ -660,7 +674,12 @@ hipError_t launch_split_heads(const DecodeArgs& a, hipStream_t stream) {
     const int64_t units = (int64_t)a.S * a.Hkv * a.B;
     if (HS * ((units + 7) / 8) * 8 > INT_MAX) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)(HS * ((units + 7) / 8) * 8));
-    hipLaunchKernelGGL((decode_split_kernel<D, BC, NT, UW, W, NSLOT, false, 1, HS>), grid, dim3(64 * W), 0, stream, a);
+    hipLaunchKernelGGL((decode_split_kernel<D, BC, NT, UW, W, NSLOT, MARGINS, 1, HS>), grid, dim3(64 * W), 0, stream, a);
+    if (MARGINS && a.vmargin != nullptr) {
+        const size_t n = (size_t)a.B * a.Hkv * a.nk;
+        hipLaunchKernelGGL(group_margin_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a.margin,
+                           a.vmargin, a.G, a.nk, n);
+    }
     return hipGetLastError();
 }
 
@@ -669,7 +688,8 @@ template <int D, int BC>
 hipError_t launch_margins_nt(const DecodeArgs& a, hipStream_t stream) {
     if (a.G <= 16) return launch_split<D, BC, 1, 16, 4, 4, true>(a, stream);
     if (a.G <= 32) return launch_split<D, BC, 2, 8, 4, 4, true>(a, stream);
-    return launch_split<D, BC, 4, 2, 4, 2, true>(a, stream);
+    if (a.G <= 64) return launch_split<D, BC, 4, 2, 4, 2, true>(a, stream);
+    return launch_split_heads<D, BC, 4, 2, 4, 2, 2, true>(a, stream);
 }
 
 template <int D, int BC>

@@ -244,8 +244,9 @@ blasst_status blasst_prefill_margins(const void* q, const void* k, float* margin
  *            max restarting at each of the num_splits splits.
  *   vmargin  fp32 [B, Hkv, ceil(N/Bc)] or NULL: the max of D over the kv
  *            group's heads (the V block is not loaded iff it is < ln(lambda)).
- * Errors and argument rules as blasst_decode (lambda absent), except that
- * gqa_ratio > 64 is UNSUPPORTED; a null margin is INVALID_ARG.
+ * Errors and argument rules as blasst_decode (lambda absent); a null margin
+ * is INVALID_ARG.  Above 64 heads per kv head, vmargin is formed by a second
+ * kernel from margin after the pass.
  */
 blasst_status blasst_decode_margins(const void* q, const void* k, float* margin, float* vmargin, int B, int Hq,
                                     int N, int d, int gqa_ratio, int Bc, int num_splits, blasst_stream_t stream);

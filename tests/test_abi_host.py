@@ -115,7 +115,7 @@ def test_prefill_margins_validation(lib, kw, status):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), 1), (dict(margin=None), 1), (dict(N=0), 1), (dict(S=0), 1), (dict(S=3), 1), (dict(G=5), 1),
-    (dict(d=80), 2), (dict(Hq=128, G=128), 2), (dict(B=0), 0), (dict(Hq=0), 0),
+    (dict(d=80), 2), (dict(Hq=256, G=256), 2), (dict(B=0), 0), (dict(Hq=0), 0),
 ])
 def test_decode_margins_validation(lib, kw, status):
     assert decode_margins(lib, **kw) == status

@@ -103,6 +103,8 @@ DECODE = [
     (1, 32, 1, 4096, 128, 128, 1, 0.02, 0),
     (2, 64, 1, 3000, 64, 128, 5, 0.02, 0),
     (1, 2, 2, 777, 128, 128, 2, 0.05, 0),
+    (1, 128, 1, 3000, 128, 128, 4, 0.02, 128),  # two 64-head workgroups per split; group max formed after
+    (2, 96, 1, 2100, 64, 64, 3, 0.02, 0),       # the second part half filled
 ]
 
 
