@@ -86,7 +86,7 @@ def parse():
                         "block sparsity")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
-    p.add_argument("--profile-target", choices=["decode", "prefill", "copy"], default=None,
+    p.add_argument("--profile-target", choices=["decode", "decode_mqa", "prefill", "copy"], default=None,
                    help="run only one kernel a few times (for hardware-counter collection) and exit")
     p.add_argument("--profile-launches", type=int, default=10)
     p.add_argument("--length-sweep", action="store_true",
@@ -109,8 +109,8 @@ def profile_target(args, lib, torch, W):
         torch.cuda.synchronize()
         print("copy: %d launches of %d bytes read + %d bytes written" % (n, COPY_BYTES, COPY_BYTES))
         return
-    if args.profile_target == "decode":
-        w = W.CONFIGS["decode_32k"]
+    if args.profile_target in ("decode", "decode_mqa"):
+        w = W.CONFIGS["decode_32k" if args.profile_target == "decode" else "decode_mqa_16k"]
         copies = [{k: dev(v) for k, v in W.generate(w).items()} for _ in range(max(1, args.copies))]
         B, Hq, N, d, Bc, S = w.B, w.Hq, w.T, w.d, w.Bc, w.num_splits
         nk = -(-N // Bc)
@@ -126,8 +126,8 @@ def profile_target(args, lib, torch, W):
                                      B, Hq, N, d, w.G, Bc, ctypes.c_double(w.lambdas[0]), 1, S, sp) == 0
         torch.cuda.synchronize()
         by = decode_bytes(w, vskip.cpu().numpy())
-        print("decode_32k: %d launches, algorithmic bytes per launch %d (read %d, written %d)" % (
-            n, by["split"], by["k"] + by["v_kept"] + B * Hq * d * 2,
+        print("%s: %d launches, algorithmic bytes per launch %d (read %d, written %d)" % (
+            w.name, n, by["split"], by["k"] + by["v_kept"] + B * Hq * d * 2,
             by["split"] - by["k"] - by["v_kept"] - B * Hq * d * 2))
         return
     w = W.CONFIGS["prefill_32k"]
