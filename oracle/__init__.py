@@ -210,7 +210,7 @@ def decode_mla(q, kv, Bc: int, lam: float, num_splits: int, scale: float, dv: in
 
     units: (b, h) units b*Hq + h (default: all).  Returns per-unit o_part [U,S,dv],
     lse_part [U,S], skip [U,nk], margin [U,nk] (skipped iff < 0); with all units also
-    o_part_full [B,Hq,S,dv], lse_part_full [B,Hq,S], skip_full [B,Hq,nk], and
+    o_part_full [B,Hq,S,dv], lse_part_full [B,Hq,S], skip_full [B,Hq,nk], margin_full [B,Hq,nk], and
     vskip_full [B,nk] / vmargin_full [B,nk]: no head kept the block (its P V is not
     formed for any head) iff vmargin < 0.
     """
@@ -238,6 +238,7 @@ def decode_mla(q, kv, Bc: int, lam: float, num_splits: int, scale: float, dv: in
         out["o_part_full"] = o_part.reshape(B, Hq, S, dv)
         out["lse_part_full"] = lse_part.reshape(B, Hq, S)
         out["skip_full"] = skip.reshape(B, Hq, nk)
+        out["margin_full"] = margin.reshape(B, Hq, nk)
         out["vskip_full"] = skip.reshape(B, Hq, nk).min(axis=1)
         out["vmargin_full"] = margin.reshape(B, Hq, nk).max(axis=1)
     return out

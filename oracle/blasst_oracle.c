@@ -35,6 +35,11 @@
  *  - a skipped block leaves (m, l, O) untouched.  This is what Eq. 1 followed
  *    by a skip gives: a skipping row has mt < m_new + ln(lambda) < m_new, hence
  *    m_new = m, so the running max does not move;
+ *  - a decision imposed through the force argument (used to adopt the other
+ *    valid decision of a block whose margin lies within float rounding of the
+ *    threshold) replaces only the keep/skip choice; the running max follows
+ *    Eq. 1 either way, and a row or split left with no kept key has o = 0,
+ *    lse = -inf;
  *  - a query row that sees no key of a visited block (possible only when the
  *    query block is taller than a KV block) votes to skip and adds nothing;
  *  - split s of S covers KV blocks [floor(s*nk/S), floor((s+1)*nk/S));
@@ -72,6 +77,24 @@ static int ceil_div(int a, int b) { return (a + b - 1) / b; }
 static void widen(const uint16_t* src, double* dst, size_t n)
 {
     for (size_t i = 0; i < n; ++i) dst[i] = bf16_value(src[i]);
+}
+
+/*
+ * Eq. 1 for a row whose block is skipped: the running max still becomes
+ * m_new = max(m, mt), and (l, O) are rescaled to it.  Under the rule's own
+ * decision a skipping row has mt < m + ln(lambda) < m, so m_new = m and nothing
+ * changes; only a decision imposed from outside (the force argument) can skip
+ * a block that raises the max, and then the max still moves, so that every
+ * later decision is taken against the prefix max of the block maxima whatever
+ * was kept before it.
+ */
+static void advance_running_max(double* m, double* l, double* o, int d, double m_new)
+{
+    if (!(m_new > *m)) return;
+    double alpha = (*m == -INFINITY) ? 0.0 : exp(*m - m_new);
+    *l *= alpha;
+    for (int e = 0; e < d; ++e) o[e] *= alpha;
+    *m = m_new;
 }
 
 /*
@@ -175,7 +198,11 @@ static void prefill_unit(const uint16_t* q, const uint16_t* k, const uint16_t* v
         if (force && force[j] >= 0) skip = force[j];
         mask[j] = (uint8_t)skip;
         margin[j] = (thr == -INFINITY) ? INFINITY : D - thr;
-        if (skip) continue;
+        if (skip) {
+            for (int r = 0; r < nr; ++r)
+                if (mt[r] > m[r]) advance_running_max(&m[r], &l[r], &acc[(size_t)r * d], d, mt[r]);
+            continue;
+        }
 
         /* Eqs. 2-4 for the kept block, every row of the query block. */
         widen(V + (size_t)c0 * d, vb, (size_t)nc * d);
@@ -187,9 +214,11 @@ static void prefill_unit(const uint16_t* q, const uint16_t* k, const uint16_t* v
         }
     }
 
+    /* A row whose kept set is empty (only a forced decision can make one)
+     * has no output: o = 0 and lse = -inf. */
     for (int r = 0; r < nr; ++r) {
-        for (int e = 0; e < d; ++e) o[(size_t)r * d + e] = acc[(size_t)r * d + e] / l[r];
-        lse[r] = m[r] + log(l[r]);
+        for (int e = 0; e < d; ++e) o[(size_t)r * d + e] = (l[r] > 0.0) ? acc[(size_t)r * d + e] / l[r] : 0.0;
+        lse[r] = (l[r] > 0.0) ? m[r] + log(l[r]) : -INFINITY;
     }
     free(qd); free(kb); free(vb); free(S); free(mt); free(m); free(l); free(acc);
 }
@@ -282,15 +311,19 @@ static void decode_unit(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                 skip[(size_t)g * nk + j] = (uint8_t)sk;
                 margin[(size_t)g * nk + j] = (thr == -INFINITY) ? INFINITY : diff - thr;
                 if (diff > best[j]) best[j] = diff;
-                if (sk) continue;
+                if (sk) {
+                    advance_running_max(&m, &l, acc, d, m_new);
+                    continue;
+                }
                 vskip[j] = 0;
                 widen(V + (size_t)c0 * d, vb, (size_t)nc * d);
                 accumulate_kept_block(&m, &l, acc, s, vb, nc, d, m_new);
             }
-            /* A split with no block (S > nk, or an empty context) contributes
-             * nothing to the merge: o = 0 and lse = -inf. */
-            for (int e = 0; e < d; ++e) o_part[((size_t)g * S + sp) * d + e] = (j1 > j0) ? acc[e] / l : 0.0;
-            lse_part[(size_t)g * S + sp] = (j1 > j0) ? m + log(l) : -INFINITY;
+            /* A split with no kept key (S > nk, an empty context, or every block
+             * skipped by a forced decision) contributes nothing to the merge:
+             * o = 0 and lse = -inf. */
+            for (int e = 0; e < d; ++e) o_part[((size_t)g * S + sp) * d + e] = (l > 0.0) ? acc[e] / l : 0.0;
+            lse_part[(size_t)g * S + sp] = (l > 0.0) ? m + log(l) : -INFINITY;
         }
     }
     for (int j = 0; j < nk; ++j) vmargin[j] = (thr == -INFINITY) ? INFINITY : best[j] - thr;
@@ -374,14 +407,17 @@ static void mla_unit(const uint16_t* q, const uint16_t* kv, int Hq, int N, int d
             if (force && force[j] >= 0) sk = force[j];
             skip[j] = (uint8_t)sk;
             margin[j] = (thr == -INFINITY) ? INFINITY : diff - thr;
-            if (sk) continue;
+            if (sk) {
+                advance_running_max(&m, &l, acc, dv, m_new);
+                continue;
+            }
             /* the value of a token is the latent part of its cache row */
             for (int c = 0; c < nc; ++c)
                 for (int e = 0; e < dv; ++e) vb[(size_t)c * dv + e] = kb[(size_t)c * dqk + e];
             accumulate_kept_block(&m, &l, acc, s, vb, nc, dv, m_new);
         }
-        for (int e = 0; e < dv; ++e) o_part[(size_t)sp * dv + e] = (j1 > j0) ? acc[e] / l : 0.0;
-        lse_part[sp] = (j1 > j0) ? m + log(l) : -INFINITY;
+        for (int e = 0; e < dv; ++e) o_part[(size_t)sp * dv + e] = (l > 0.0) ? acc[e] / l : 0.0;
+        lse_part[sp] = (l > 0.0) ? m + log(l) : -INFINITY;
     }
     free(qd); free(kb); free(vb); free(s); free(acc);
 }
