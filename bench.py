@@ -81,9 +81,11 @@ def parse():
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-mla", action="store_true")
     p.add_argument("--all-configs", action="store_true",
-                   help="also time every workload configuration (prefill_1k_tiny, decode_128k_b16, decode_mqa_16k "
-                        "besides the two 32K ones) and two ragged batches: time, fraction of the roofline, "
-                        "block sparsity")
+                   help="(the default) also time every other workload configuration (prefill_1k_tiny, "
+                        "decode_128k_b16, decode_mqa_16k besides the two 32K ones) and two ragged batches: time, "
+                        "fraction of the roofline, block sparsity")
+    p.add_argument("--no-other-configs", action="store_true",
+                   help="skip the other workload configurations and the ragged batches")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--profile-target", choices=["decode", "decode_mqa", "prefill", "copy"], default=None,
@@ -571,6 +573,9 @@ def bench_mla(args, lib, torch, W):
         nk = -(-N // Bc)
         skip = torch.empty((B, Hq, nk), dtype=torch.uint8, device="cuda")
         hg = 64 if Hq % 64 == 0 else 32
+        # the unit whose P V product a block skips only when every head in it skips: a 16-head
+        # tile in the 64-head pipeline, the whole 32-head workgroup in the 32-head kernel
+        tile = 16 if hg == 64 else 32
         out = {}
         for lam in (0.0,) + tuple(w.lambdas):
             args_ = [(P(q), P(kv), P(o_part), P(lse_part), P(skip), B, Hq, N, dqk, dv, Bc,
@@ -589,21 +594,21 @@ def bench_mla(args, lib, torch, W):
                 torch.cuda.synchronize()
                 ts.append(s0.elapsed_time(s1) * 1e3 / 20)
             us = float(np.median(ts))
-            sk = skip.cpu().numpy().astype(bool)                      # [B, Hq, nk]
-            group_kept = ~sk.reshape(B, Hq // hg, hg, nk).all(axis=2)  # P V formed for the group
-            rows = np.minimum(Bc, N - Bc * np.arange(nk))              # tokens per block
+            sk = skip.cpu().numpy().astype(bool)                          # [B, Hq, nk]
+            tile_kept = ~sk.reshape(B, Hq // tile, tile, nk).all(axis=2)  # P V formed for the tile
+            rows = np.minimum(Bc, N - Bc * np.arange(nk))                  # tokens per block
             s_flops = 2.0 * dqk * N * Hq * B
-            pv_flops = 2.0 * dv * hg * float((group_kept * rows).sum())
+            pv_flops = 2.0 * dv * tile * float((tile_kept * rows).sum())
             by = B * N * dqk * 2 + B * Hq * dqk * 2 + B * Hq * S * (dv + 1) * 4 + B * Hq * nk
             out["%g" % lam] = dict(us=round(us, 2), us_min=round(min(ts), 2), us_max=round(max(ts), 2),
                                    GBs=round(by / us / 1e3, 1), frac_of_hbm_peak=round(by / us / 1e3 / HBM_PEAK_GBS, 4),
                                    tflops_executed=round((s_flops + pv_flops) / us / 1e6, 1),
                                    block_sparsity=round(float(sk.mean()), 5),
-                                   pv_skipped_fraction=round(1.0 - float(group_kept.mean()), 5))
+                                   pv_skipped_fraction=round(1.0 - float(tile_kept.mean()), 5))
         dense = out["0"]["us"]
         for v in out.values():
             v["speedup_vs_lambda0"] = round(dense / v["us"], 4)
-        by_block["Bc%d" % Bc] = dict(heads_per_workgroup=hg, by_lambda=out)
+        by_block["Bc%d" % Bc] = dict(heads_per_workgroup=hg, pv_skip_unit_heads=tile, by_lambda=out)
     by = B * N * dqk * 2
     return dict(workload=w.name, B=B, Hq=Hq, d_qk=dqk, d_v=dv, context=N, num_splits=S, by_block=by_block,
                 hbm_roofline_us=round(by / (HBM_PEAK_GBS * 1e3), 2),
@@ -621,11 +626,22 @@ def cpu_model():
     return None
 
 
+def oracle_threads():
+    """Threads for the oracle: the host's CPU share for one GPU (OMP_NUM_THREADS where the job
+    sets it), never more than the CPUs this process may run on."""
+    affinity = len(os.sched_getaffinity(0))
+    try:
+        share = int(os.environ.get("OMP_NUM_THREADS", "16"))
+    except ValueError:
+        share = 16
+    return max(1, min(share, affinity))
+
+
 def cpu_baseline(args, dres):
     import oracle
     w = dres["w"]
     x = dres["x"]
-    threads = min(16, len(os.sched_getaffinity(0)))
+    threads = oracle_threads()
     oracle.decode(x["q"], x["k"], x["v"], w.Bc, w.lambdas[0], w.num_splits, threads=threads)  # warm
     n, t0 = 0, time.perf_counter()
     while True:
@@ -650,7 +666,10 @@ def cpu_baseline(args, dres):
     one_prefill = time.perf_counter() - t1
     return dict(value=round(gbs, 4), unit="GB/s", cores=threads, kind="oracle",
                 sample="full decode_32k step (all 32 heads, 16 splits) + combine, repeated %d times in %.1f s; "
-                       "%.1f ms per step" % (n, el, per * 1e3),
+                       "%.1f ms per step; one task per (sequence, query head, split): %d tasks on %d threads"
+                       % (n, el, per * 1e3, w.B * w.Hq * w.num_splits, threads),
+                threads=threads, host_logical_cpus=os.cpu_count(), affinity_cpus=len(os.sched_getaffinity(0)),
+                omp_num_threads_env=os.environ.get("OMP_NUM_THREADS"),
                 cpu_model=cpu_model(),
                 single_thread_s={"decode_32k_step": round(one_decode, 3), "prefill_1k_tiny": round(one_prefill, 3)})
 
@@ -680,7 +699,7 @@ def main():
     pre = None if args.no_prefill else bench_prefill(args, lib, torch, W)
     mla = None if args.no_mla else bench_mla(args, lib, torch, W)
     configs = None
-    if args.all_configs:
+    if not args.no_other_configs:
         configs = {}
         for name in ("prefill_1k_tiny", "decode_128k_b16", "decode_mqa_16k"):
             configs[name] = bench_config(name, args, lib, torch, W)

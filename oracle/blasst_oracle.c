@@ -255,83 +255,83 @@ int oracle_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 /* ------------------------------------------------------------------------ */
 
 /*
- * All G query heads of kv head (b, hkv): unit = b*Hkv + hkv.  One query row per
- * head; every key of the context is visible.  Per-unit outputs:
+ * One split of one query head: the G query heads of kv head (b, hkv) form
+ * unit = b*Hkv + hkv; this computes head g of the unit over split sp, whose
+ * blocks are [floor(sp*nk/S), floor((sp+1)*nk/S)).  One query row; every key of
+ * the context is visible.  Outputs for (g, sp):
+ *   o_part  [d]   the split's normalised output
+ *   lse_part[1]   the split's m + ln(l)
+ *   skip    the head's row [nk]: entries of the split's blocks, 1 = skipped
+ *   margin  the head's row [nk]: (mt - m_new) - ln(lambda), skipped iff < 0
+ * force (nullable): the head's row [nk], -1 = own decision, 0 = keep, 1 = skip.
+ */
+static void decode_head_split(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                              int Hq, int Hkv, int N, int d, int Bc, double thr, int S,
+                              int64_t unit, int g, int sp, const int8_t* force, double* o_part,
+                              double* lse_part, uint8_t* skip, double* margin)
+{
+    const int G = Hq / Hkv;
+    const int nk = ceil_div(N, Bc);
+    const int hkv = (int)(unit % Hkv), b = (int)(unit / Hkv);
+    const int hq = hkv * G + g;
+    const double scale = 1.0 / sqrt((double)d);
+    const uint16_t* K = k + ((size_t)b * Hkv + hkv) * (size_t)N * d;
+    const uint16_t* V = v + ((size_t)b * Hkv + hkv) * (size_t)N * d;
+    const int j0 = (int)((int64_t)sp * nk / S), j1 = (int)((int64_t)(sp + 1) * nk / S);
+
+    double* qd = malloc(sizeof(double) * d);
+    double* kb = malloc(sizeof(double) * (size_t)Bc * d);
+    double* vb = malloc(sizeof(double) * (size_t)Bc * d);
+    double* s = malloc(sizeof(double) * Bc);
+    double* acc = calloc(d, sizeof(double));
+    widen(q + ((size_t)b * Hq + hq) * d, qd, d);
+
+    double m = -INFINITY, l = 0.0;
+    for (int j = j0; j < j1; ++j) {
+        const int c0 = j * Bc, nc = (N - c0 < Bc) ? N - c0 : Bc;
+        widen(K + (size_t)c0 * d, kb, (size_t)nc * d);
+        /* S = q K_j^T / sqrt(d) — always formed. */
+        double row_max = -INFINITY;
+        for (int c = 0; c < nc; ++c) {
+            double dot = 0.0;
+            for (int e = 0; e < d; ++e) dot += qd[e] * kb[(size_t)c * d + e];
+            s[c] = dot * scale;
+            if (s[c] > row_max) row_max = s[c];
+        }
+        /* Eq. 1 then Eq. 5 for the single row. */
+        double m_new = (m > row_max) ? m : row_max;
+        double diff = row_max - m_new;
+        int sk = diff < thr;
+        if (force && force[j] >= 0) sk = force[j];
+        skip[j] = (uint8_t)sk;
+        margin[j] = (thr == -INFINITY) ? INFINITY : diff - thr;
+        if (sk) {
+            advance_running_max(&m, &l, acc, d, m_new);
+            continue;
+        }
+        widen(V + (size_t)c0 * d, vb, (size_t)nc * d);
+        accumulate_kept_block(&m, &l, acc, s, vb, nc, d, m_new);
+    }
+    /* A split with no kept key (S > nk, an empty context, or every block
+     * skipped by a forced decision) contributes nothing to the merge:
+     * o = 0 and lse = -inf. */
+    for (int e = 0; e < d; ++e) o_part[e] = (l > 0.0) ? acc[e] / l : 0.0;
+    *lse_part = (l > 0.0) ? m + log(l) : -INFINITY;
+    free(qd); free(kb); free(vb); free(s); free(acc);
+}
+
+/*
+ * Split-KV decode over a list of (b, hkv) units; q [B,Hq,1,d], k and v [B,Hkv,N,d].
+ * Per-unit outputs:
  *   o_part  [G, S, d]  each split's normalised output
  *   lse_part[G, S]     each split's m + ln(l)
  *   skip    [G, nk]    1 = the head's row skipped the block
  *   vskip   [nk]       1 = no head of the group kept the block (its V is not needed)
  *   margin  [G, nk]    (mt - m_new) - ln(lambda); skipped iff < 0
  *   vmargin [nk]       max over heads of (mt - m_new) - ln(lambda)
- * force (nullable) [G, nk]: -1 = own decision, 0 = keep, 1 = skip.
- */
-static void decode_unit(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                        int Hq, int Hkv, int N, int d, int Bc, double thr, int S,
-                        int64_t unit, const int8_t* force, double* o_part, double* lse_part,
-                        uint8_t* skip, uint8_t* vskip, double* margin, double* vmargin)
-{
-    const int G = Hq / Hkv;
-    const int nk = ceil_div(N, Bc);
-    const int hkv = (int)(unit % Hkv), b = (int)(unit / Hkv);
-    const double scale = 1.0 / sqrt((double)d);
-    const uint16_t* K = k + ((size_t)b * Hkv + hkv) * (size_t)N * d;
-    const uint16_t* V = v + ((size_t)b * Hkv + hkv) * (size_t)N * d;
-
-    double* qd = malloc(sizeof(double) * d);
-    double* kb = malloc(sizeof(double) * (size_t)Bc * d);
-    double* vb = malloc(sizeof(double) * (size_t)Bc * d);
-    double* s = malloc(sizeof(double) * Bc);
-    double* acc = malloc(sizeof(double) * d);
-    double* best = malloc(sizeof(double) * nk);
-    for (int j = 0; j < nk; ++j) { vskip[j] = 1; best[j] = -INFINITY; }
-
-    for (int g = 0; g < G; ++g) {
-        const int hq = hkv * G + g;
-        widen(q + ((size_t)b * Hq + hq) * d, qd, d);
-        for (int sp = 0; sp < S; ++sp) {
-            const int j0 = (int)((int64_t)sp * nk / S), j1 = (int)((int64_t)(sp + 1) * nk / S);
-            double m = -INFINITY, l = 0.0;
-            for (int e = 0; e < d; ++e) acc[e] = 0.0;
-            for (int j = j0; j < j1; ++j) {
-                const int c0 = j * Bc, nc = (N - c0 < Bc) ? N - c0 : Bc;
-                widen(K + (size_t)c0 * d, kb, (size_t)nc * d);
-                /* S = q K_j^T / sqrt(d) — always formed. */
-                double row_max = -INFINITY;
-                for (int c = 0; c < nc; ++c) {
-                    double dot = 0.0;
-                    for (int e = 0; e < d; ++e) dot += qd[e] * kb[(size_t)c * d + e];
-                    s[c] = dot * scale;
-                    if (s[c] > row_max) row_max = s[c];
-                }
-                /* Eq. 1 then Eq. 5 for the single row. */
-                double m_new = (m > row_max) ? m : row_max;
-                double diff = row_max - m_new;
-                int sk = diff < thr;
-                if (force && force[(size_t)g * nk + j] >= 0) sk = force[(size_t)g * nk + j];
-                skip[(size_t)g * nk + j] = (uint8_t)sk;
-                margin[(size_t)g * nk + j] = (thr == -INFINITY) ? INFINITY : diff - thr;
-                if (diff > best[j]) best[j] = diff;
-                if (sk) {
-                    advance_running_max(&m, &l, acc, d, m_new);
-                    continue;
-                }
-                vskip[j] = 0;
-                widen(V + (size_t)c0 * d, vb, (size_t)nc * d);
-                accumulate_kept_block(&m, &l, acc, s, vb, nc, d, m_new);
-            }
-            /* A split with no kept key (S > nk, an empty context, or every block
-             * skipped by a forced decision) contributes nothing to the merge:
-             * o = 0 and lse = -inf. */
-            for (int e = 0; e < d; ++e) o_part[((size_t)g * S + sp) * d + e] = (l > 0.0) ? acc[e] / l : 0.0;
-            lse_part[(size_t)g * S + sp] = (l > 0.0) ? m + log(l) : -INFINITY;
-        }
-    }
-    for (int j = 0; j < nk; ++j) vmargin[j] = (thr == -INFINITY) ? INFINITY : best[j] - thr;
-    free(qd); free(kb); free(vb); free(s); free(acc); free(best);
-}
-
-/*
- * Split-KV decode over a list of (b, hkv) units; q [B,Hq,1,d], k and v [B,Hkv,N,d].
+ * force (nullable) [U, G, nk]: -1 = own decision, 0 = keep, 1 = skip.
+ * Every (unit, head, split) is independent and runs as its own task; the group
+ * outputs (vskip, vmargin) are formed from the heads' rows afterwards.
  * Returns 0, or -1 on a bad argument.
  */
 int oracle_decode(const uint16_t* q, const uint16_t* k, const uint16_t* v,
@@ -345,16 +345,33 @@ int oracle_decode(const uint16_t* q, const uint16_t* k, const uint16_t* v,
     const int nk = ceil_div(N, Bc), G = Hq / Hkv, S = num_splits;
     if (S < 1) return -1;
     const double thr = log_threshold(lambda);
+    const int64_t tasks = (int64_t)n_units * G * S;
 #ifdef _OPENMP
     if (nthreads > 0) omp_set_num_threads(nthreads);
 #pragma omp parallel for schedule(dynamic, 1)
 #endif
+    for (int64_t t = 0; t < tasks; ++t) {
+        const int sp = (int)(t % S), g = (int)((t / S) % G);
+        const int64_t u = t / ((int64_t)S * G);
+        const size_t row = (size_t)u * G + g;  /* the head's row among the units' heads */
+        decode_head_split(q, k, v, Hq, Hkv, N, d, Bc, thr, S, units[u], g, sp,
+                          force ? force + row * nk : NULL, o_part + (row * S + sp) * d,
+                          lse_part + row * S + sp, skip + row * nk, margin + row * nk);
+    }
+    /* V is needed for a block iff some head of the group keeps it; the group's
+     * margin is the largest of its heads' margins. */
     for (int u = 0; u < n_units; ++u) {
-        decode_unit(q, k, v, Hq, Hkv, N, d, Bc, thr, S, units[u],
-                    force ? force + (size_t)u * G * nk : NULL,
-                    o_part + (size_t)u * G * S * d, lse_part + (size_t)u * G * S,
-                    skip + (size_t)u * G * nk, vskip + (size_t)u * nk,
-                    margin + (size_t)u * G * nk, vmargin + (size_t)u * nk);
+        for (int j = 0; j < nk; ++j) {
+            uint8_t all_skip = 1;
+            double best = -INFINITY;
+            for (int g = 0; g < G; ++g) {
+                const size_t row = (size_t)u * G + g;
+                all_skip &= skip[row * nk + j];
+                if (margin[row * nk + j] > best) best = margin[row * nk + j];
+            }
+            vskip[(size_t)u * nk + j] = all_skip;
+            vmargin[(size_t)u * nk + j] = best;
+        }
     }
     return 0;
 }

@@ -3,7 +3,8 @@
 Small shapes cover the edge cases (ragged tails, one block per split, MHA /
 GQA / MQA head mapping, d and Bc in {64, 128}, lambda from 0 to 0.5, T < Bc);
 the five workload configurations run at full size, compared on every output
-where the oracle is cheap and on sampled units where it is not.
+where the oracle is cheap, on whole heads at the 32K prefill, and on sampled
+kv groups of the large decode batches.
 """
 import sys
 
@@ -44,6 +45,14 @@ DECODE_SMALL = [
     (2, 40, 2, 2500, 128, 64, 3, 0.02, 0),     # G = 20: a partly filled 32-head tile
     (1, 128, 1, 3000, 128, 128, 4, 0.02, 128), # G = 128: two 64-head workgroups per split, ragged
     (2, 96, 1, 2100, 64, 64, 3, 0.02, 0),      # G = 96: the second 64-head part half filled
+    # up to 16 heads, 129-256 (b, kv head, split) units: one 8-wave workgroup per split, two V slots
+    (2, 32, 8, 4096, 128, 128, 16, 0.01, 128), # 256 units
+    (1, 8, 2, 9000, 64, 64, 80, 0.02, 0),      # 160 units, 1-2 blocks per split, ragged N
+    (2, 12, 3, 3000, 128, 64, 24, 0.02, 64),   # 144 units, G = 4, d = 128 with Bc = 64
+    # up to 16 heads, more than 256 units: one 4-wave workgroup per split, four slots per wave
+    (4, 16, 4, 5000, 64, 64, 20, 0.02, 64),    # 320 units, d = Bc = 64, ragged N
+    (3, 8, 8, 3000, 128, 64, 12, 0.02, 0),     # 288 units, MHA, d = 128 with Bc = 64
+    (6, 16, 4, 3000, 64, 128, 12, 0.02, 0),    # 288 units, d = 64 with Bc = 128
 ]
 
 
@@ -106,13 +115,22 @@ def prefill_32k():
     return w, x, {k: to_device(v) for k, v in x.items()}
 
 
+# two whole query heads per lambda, from different kv groups (every query block,
+# every mask entry, every output row), and single query blocks of other heads
+WHOLE_HEADS = {1e-4: (0, 29), 1e-3: (10, 19), 1e-2: (5, 30)}
+
+
 @pytest.mark.parametrize("lam", [1e-4, 1e-3, 1e-2])
-def test_config_prefill_32k_sampled(prefill_32k, lam):
+def test_config_prefill_32k(prefill_32k, lam):
     w, x, x_dev = prefill_32k
     nq = w.T // w.Bc
-    picks = [(0, nq - 1), (7, nq - 2), (13, nq // 2), (31, 0), (20, 64), (3, 200), (26, 1), (31, nq - 1)]
-    units = [hq * nq + i for hq, i in picks]
-    say(w.name, "lambda", lam, "units", picks)
+    heads = WHOLE_HEADS[lam]
+    assert len({h // w.G for h in heads}) == len(heads)
+    picks = [(7, nq - 2), (13, nq // 2), (31, 0), (20, 64), (3, 200), (26, 1), (31, nq - 1)]
+    picks = [(h, i) for h, i in picks if h not in heads]
+    # heaviest query blocks first, so the oracle's threads finish together
+    units = [h * nq + i for h in heads for i in reversed(range(nq))] + [h * nq + i for h, i in picks]
+    say(w.name, "lambda", lam, "whole heads", heads, "single query blocks", picks)
     gpu = run_gpu_prefill(x_dev, w.Bc, lam)
     mask = gpu["mask"].cpu().numpy()
     # properties over every decision of the full problem
@@ -123,6 +141,7 @@ def test_config_prefill_32k_sampled(prefill_32k, lam):
     say("  sparsity %.4f" % float((mask[:, :, tri] == 1).mean()))
     rep = check_prefill(x, w.Bc, lam, units=units, gpu=gpu)
     say(" ", rep)
+    assert rep.decisions == len(heads) * nq * (nq + 1) // 2 + sum(i + 1 for _, i in picks)
 
 
 def test_config_decode_128k_b16_sampled():

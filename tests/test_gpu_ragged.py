@@ -116,6 +116,9 @@ DECODE = [
     (4, 16, 1, 1536, 128, 64, 8, 0, [1536, 700, 300, 1]),
     (2, 8, 2, 40960, 128, 128, 8, 256, [40960, 23000]),      # paired workgroups, several phases per split
     (3, 128, 1, 1500, 128, 128, 4, 0, [1500, 0, 333]),         # G = 128: two head parts per split
+    (2, 32, 8, 4096, 128, 128, 16, 128, [4096, 2000]),         # 256 units: one 8-wave workgroup per split
+    (2, 8, 2, 9000, 64, 64, 40, 0, [9000, 3000]),              # 160 units at d = Bc = 64
+    (6, 16, 4, 3000, 64, 128, 12, 0, [3000, 0, 1, 2999, 1500, 128]),  # 288 units: 4-wave workgroups, d = 64
 ]
 
 
