@@ -86,10 +86,15 @@ def parse():
                         "fraction of the roofline, block sparsity")
     p.add_argument("--no-other-configs", action="store_true",
                    help="skip the other workload configurations and the ragged batches")
+    p.add_argument("--no-length-sweep-timing", action="store_true",
+                   help="skip the decode timing of the 128K length-sweep sequences at lambda = a/L")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
-    p.add_argument("--profile-target", choices=["decode", "decode_mqa", "prefill", "copy"], default=None,
+    p.add_argument("--profile-target", choices=["decode", "decode_mqa", "decode_dense", "decode_ceiling",
+                                                 "decode_sweep128", "prefill", "copy"], default=None,
                    help="run only one kernel a few times (for hardware-counter collection) and exit")
+    p.add_argument("--profile-lambda", type=float, default=None,
+                   help="lambda for --profile-target decode_sweep128 (default: the split kernel's lambda = 0)")
     p.add_argument("--profile-launches", type=int, default=10)
     p.add_argument("--length-sweep", action="store_true",
                    help="instead of the bench: sparsity drift over 4K-128K context and the lambda = a/L calibration")
@@ -111,9 +116,34 @@ def profile_target(args, lib, torch, W):
         torch.cuda.synchronize()
         print("copy: %d launches of %d bytes read + %d bytes written" % (n, COPY_BYTES, COPY_BYTES))
         return
-    if args.profile_target in ("decode", "decode_mqa"):
-        w = W.CONFIGS["decode_32k" if args.profile_target == "decode" else "decode_mqa_16k"]
+    if args.profile_target in ("decode_dense", "decode_ceiling"):
+        w = W.CONFIGS["decode_32k"]
         copies = [{k: dev(v) for k, v in W.generate(w).items()} for _ in range(max(1, args.copies))]
+        B, Hq, N, d, Bc, S = w.B, w.Hq, w.T, w.d, w.Bc, w.num_splits
+        o_part = torch.empty((B, Hq, S, d), dtype=torch.float32, device="cuda")
+        lse_part = torch.empty((B, Hq, S), dtype=torch.float32, device="cuda")
+        sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+        for i in range(n):
+            c = copies[i % len(copies)]
+            if args.profile_target == "decode_dense":
+                st = lib.blasst_decode_dense(P(c["q"]), P(c["k"]), P(c["v"]), P(o_part), P(lse_part), B, Hq, N, d, w.G,
+                                             Bc, S, sp)
+            else:
+                st = lib.blasst_decode_load_ceiling(P(c["k"]), P(c["v"]), B, w.Hkv, N, d, Bc, S, sp)
+            assert st == 0
+        torch.cuda.synchronize()
+        print("%s on %s: %d launches; K + V bytes per launch %d" % (args.profile_target, w.name, n,
+                                                                  2 * B * w.Hkv * N * d * 2))
+        return
+    if args.profile_target in ("decode", "decode_mqa", "decode_sweep128"):
+        if args.profile_target == "decode_sweep128":
+            w = W.sweep_workload("decode", W.SWEEP_LENGTHS[-1], "evaluation").with_(num_splits=SWEEP128_SPLITS)
+            w = w.with_(lambdas=(args.profile_lambda or 0.0,))
+        else:
+            w = W.CONFIGS["decode_32k" if args.profile_target == "decode" else "decode_mqa_16k"]
+        ncopies = 1 if args.profile_target == "decode_sweep128" else max(1, args.copies)
+        copies = [{k: dev(v) for k, v in W.generate(w).items()} for _ in range(ncopies)]
         B, Hq, N, d, Bc, S = w.B, w.Hq, w.T, w.d, w.Bc, w.num_splits
         nk = -(-N // Bc)
         o_part = torch.empty((B, Hq, S, d), dtype=torch.float32, device="cuda")
@@ -128,9 +158,10 @@ def profile_target(args, lib, torch, W):
                                      B, Hq, N, d, w.G, Bc, ctypes.c_double(w.lambdas[0]), 1, S, sp) == 0
         torch.cuda.synchronize()
         by = decode_bytes(w, vskip.cpu().numpy())
-        print("%s: %d launches, algorithmic bytes per launch %d (read %d, written %d)" % (
-            w.name, n, by["split"], by["k"] + by["v_kept"] + B * Hq * d * 2,
-            by["split"] - by["k"] - by["v_kept"] - B * Hq * d * 2))
+        print("%s at lambda %g: %d launches, algorithmic bytes per launch %d (read %d, written %d); "
+              "V-load sparsity %.4f" % (w.name, w.lambdas[0], n, by["split"], by["k"] + by["v_kept"] + B * Hq * d * 2,
+                                       by["split"] - by["k"] - by["v_kept"] - B * Hq * d * 2,
+                                       float(vskip.cpu().numpy().mean())))
         return
     w = W.CONFIGS["prefill_32k"]
     x = {k: dev(v) for k, v in W.generate(w).items()}
@@ -149,6 +180,8 @@ def profile_target(args, lib, torch, W):
 
 
 SWEEP_LAMBDAS = tuple(float(x) for x in np.geomspace(1e-5, 0.9, 50))  # candidate thresholds
+DECODE_SWEEP_LAMBDAS = (0.0, 1e-3, 1e-2, 1e-1, 0.5)  # decode_32k inputs, split kernel against the dense one
+SWEEP128_SPLITS = 4  # splits of the timed 128K length-sweep decode
 SWEEP_FIXED = (1e-3, 3e-3)
 SWEEP_TARGETS = (0.5, 0.7)
 
@@ -281,39 +314,80 @@ def bench_decode(args, lib, torch, W):
         trials.append(start.elapsed_time(stop) / args.steps)
     split_ms = float(np.median(trials))
 
-    # dense-equivalent reference (lambda = 0): same kernels, nothing skipped
-    for s in range(args.warmup):
-        check(decode_fn(*dense_args[s % len(dense_args)]))
-    torch.cuda.synchronize()
-    start.record(stream)
-    for s in range(args.steps):
-        check(decode_fn(*dense_args[s % len(dense_args)]))
-        check(combine_fn(*comb))
-    stop.record(stream)
-    torch.cuda.synchronize()
-    dense_step_ms = start.elapsed_time(stop) / args.steps
+    def step_time(fn_args):
+        """Time of one step (kernel + combine) over K back-to-back steps, after W warm-up steps."""
+        for s in range(args.warmup):
+            fn_args(s)
+            check(combine_fn(*comb))
+        torch.cuda.synchronize()
+        start.record(stream)
+        for s in range(args.steps):
+            fn_args(s)
+            check(combine_fn(*comb))
+        stop.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / args.steps
 
-    # the dense reference: no block ever skipped and no decision bytes (blasst_decode_dense)
+    def kernel_trials(fn_args, reps):
+        """TRIALS trials of reps back-to-back launches of one kernel: median, min, max in ms."""
+        for s in range(4):
+            fn_args(s)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(TRIALS):
+            start.record(stream)
+            for s in range(reps):
+                fn_args(s)
+            stop.record(stream)
+            torch.cuda.synchronize()
+            ts.append(start.elapsed_time(stop) / reps)
+        return float(np.median(ts)), min(ts), max(ts)
+
+    # the same kernel at lambda = 0 (nothing skipped; the test and the decision bytes still run)
+    lambda0_step_ms = step_time(lambda s: check(decode_fn(*dense_args[s % len(dense_args)])))
+    # the dense kernel (blasst_decode_dense: one pass over K and V, no decision)
     ref_args = [(P(c["q"]), P(c["k"]), P(c["v"]), P(o_part), P(lse_part), B, Hq, N, d, w.G, Bc, S, sp) for c in copies]
-    for s in range(args.warmup):
-        check(lib.blasst_decode_dense(*ref_args[s % len(ref_args)]))
-    torch.cuda.synchronize()
-    start.record(stream)
-    for s in range(args.steps):
-        check(lib.blasst_decode_dense(*ref_args[s % len(ref_args)]))
-        check(combine_fn(*comb))
-    stop.record(stream)
-    torch.cuda.synchronize()
-    ref_step_ms = start.elapsed_time(stop) / args.steps
+    ref_fn = lambda s: check(lib.blasst_decode_dense(*ref_args[s % len(ref_args)]))  # noqa: E731
+    dense_step_ms = step_time(ref_fn)
+    reps = max(args.steps, 50)
+    dense_kernel_ms = kernel_trials(ref_fn, reps)
+    # the split kernel's loads alone at lambda = 0 (blasst_decode_load_ceiling): the floor its bytes and
+    # its access pattern set on this part
+    ceil_args = [(P(c["k"]), P(c["v"]), B, w.Hkv, N, d, Bc, S, sp) for c in copies]
+    load_ceiling_ms = kernel_trials(lambda s: check(lib.blasst_decode_load_ceiling(*ceil_args[s % len(ceil_args)])),
+                                    reps)
 
     # decisions of the timed configuration (identical on every copy)
     check(decode_fn(*sargs[0]))
     torch.cuda.synchronize()
     sk, vsk = skip.cpu().numpy(), vskip.cpu().numpy()
     by = decode_bytes(w, vsk)
-    return dict(w=w, x=x, step_ms=step_ms, split_ms=split_ms, split_trials_ms=trials, dense_step_ms=dense_step_ms,
-                ref_step_ms=ref_step_ms, wall=wall, bytes=by, block_sparsity=float(sk.mean()),
-                vload_sparsity=float(vsk.mean()))
+
+    # lambda sweep on the same inputs: the split kernel against the dense kernel
+    sweep = []
+    dense_by = decode_bytes(w, np.zeros_like(vsk))
+    for lam_ in DECODE_SWEEP_LAMBDAS:
+        la = [split_args(c, lam_) for c in copies]
+        ms = kernel_trials(lambda s: check(decode_fn(*la[s % len(la)])), reps)
+        check(decode_fn(*la[0]))
+        torch.cuda.synchronize()
+        sk_, vsk_ = skip.cpu().numpy(), vskip.cpu().numpy()
+        by_ = decode_bytes(w, vsk_)
+        sweep.append(dict(
+            lam=lam_, split_kernel_us=round(ms[0] * 1e3, 3), split_kernel_us_min=round(ms[1] * 1e3, 3),
+            split_kernel_us_max=round(ms[2] * 1e3, 3), block_sparsity=round(float(sk_.mean()), 5),
+            vload_sparsity=round(float(vsk_.mean()), 5), bytes_per_launch=by_["split"],
+            GBs=round(by_["split"] / (ms[0] * 1e-3) / 1e9, 1),
+            frac_of_hbm_peak=round(by_["split"] / (ms[0] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            speedup_vs_dense_kernel=round(dense_kernel_ms[0] / ms[0], 4),
+            bytes_ratio_dense_over_this=round(dense_by["split"] / by_["split"], 4)))
+    l0 = next(r for r in sweep if r["lam"] == 0.0)["split_kernel_us"]
+    for r in sweep:
+        r["speedup_vs_lambda0"] = round(l0 / r["split_kernel_us"], 4)
+    return dict(w=w, x=x, step_ms=step_ms, split_ms=split_ms, split_trials_ms=trials, lambda0_step_ms=lambda0_step_ms,
+                dense_step_ms=dense_step_ms, dense_kernel_ms=dense_kernel_ms, load_ceiling_ms=load_ceiling_ms,
+                wall=wall, bytes=by,
+                block_sparsity=float(sk.mean()), vload_sparsity=float(vsk.mean()), lambda_sweep=sweep)
 
 
 def bench_prefill(args, lib, torch, W):
@@ -553,6 +627,90 @@ def bench_ragged(args, lib, torch, W):
     return {"decode_serving_batch": dec, "prefill_causal": pre}
 
 
+def calibrate_decode_policy(W, bsa, B=None):
+    """lambda = a/L for decode, fitted on the calibration sequences of the length-sweep family
+    (4K-64K, one split, GPU margins): returns (alpha, beta, number of points)."""
+    from block_sparse_attention_flash_amd import policy
+    lengths = W.SWEEP_LENGTHS[:5]
+    margins = [sweep_margins("decode", L, "calibration", W, bsa, B)[0] for L in lengths]
+    a, s = policy.calibration_points(margins, list(lengths), SWEEP_LAMBDAS)
+    alpha, beta = policy.fit_exponential(a, s)
+    return alpha, beta, int(len(a))
+
+
+def bench_decode_length_sweep(args, lib, torch, W, bsa):
+    """What a decode skip buys where skipping is common: the length-sweep family's held-out 128K
+    sequences (B = 4, Hq = 32, Hkv = 8, d = 128), split 4 ways (128 units: the two-workgroups-per-split
+    layout fills the GPU, and each split's running max sees 256 blocks, close to the one-split margins
+    the policy is fitted on; a split restarts the max, so 16 splits skip far less), timed through the split kernel at
+    lambda = a/L for 50% and 70% target sparsity (a fitted on the 4K-64K calibration sequences) and at
+    fixed lambdas, against lambda = 0 and the dense kernel.  The split kernel reads all of K and the kept
+    V blocks, so the bytes predict the speed-up: 1 / (1 - vload * V / (K + V))."""
+    from block_sparse_attention_flash_amd import policy
+    alpha, beta, npts = calibrate_decode_policy(W, bsa)
+    L = W.SWEEP_LENGTHS[-1]
+    w = W.sweep_workload("decode", L, "evaluation").with_(num_splits=SWEEP128_SPLITS)
+    x = {k: dev(v) for k, v in W.generate(w).items()}
+    B, Hq, N, d, Bc, S = w.B, w.Hq, w.T, w.d, w.Bc, w.num_splits
+    nk = -(-N // Bc)
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    o_part = torch.empty((B, Hq, S, d), dtype=torch.float32, device="cuda")
+    lse_part = torch.empty((B, Hq, S), dtype=torch.float32, device="cuda")
+    skip = torch.empty((B, Hq, nk), dtype=torch.uint8, device="cuda")
+    vskip = torch.empty((B, w.Hkv, nk), dtype=torch.uint8, device="cuda")
+
+    def ok(st):
+        if st != 0:
+            raise RuntimeError("libblasst call failed with status %d" % st)
+
+    def trials(fn, reps=20):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(TRIALS):
+            s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s0.record(stream)
+            for _ in range(reps):
+                fn()
+            s1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(s0.elapsed_time(s1) / reps)
+        return float(np.median(ts)), min(ts), max(ts)
+
+    dense_ms = trials(lambda: ok(lib.blasst_decode_dense(P(x["q"]), P(x["k"]), P(x["v"]), P(o_part), P(lse_part),
+                                                          B, Hq, N, d, w.G, Bc, S, sp)))
+    targets = {"a/L, 50%": policy.lambda_for(0.5, L, alpha, beta), "a/L, 70%": policy.lambda_for(0.7, L, alpha, beta)}
+    points = [("lambda = 0", 0.0), ("fixed 1e-3", 1e-3), ("fixed 3e-3", 3e-3)] + list(targets.items())
+    dense_bytes = decode_bytes(w, np.zeros((B, w.Hkv, nk), np.uint8))["split"]
+    rows = []
+    for label, lam in points:
+        a = (P(x["q"]), P(x["k"]), P(x["v"]), P(o_part), P(lse_part), P(skip), P(vskip), B, Hq, N, d, w.G, Bc,
+             ctypes.c_double(lam), 1, S, sp)
+        ms = trials(lambda: ok(lib.blasst_decode(*a)))
+        ok(lib.blasst_decode(*a))
+        torch.cuda.synchronize()
+        sk, vsk = skip.cpu().numpy(), vskip.cpu().numpy()
+        by = decode_bytes(w, vsk)["split"]
+        rows.append(dict(point=label, lam=lam, split_kernel_us=round(ms[0] * 1e3, 2),
+                         split_kernel_us_min=round(ms[1] * 1e3, 2), split_kernel_us_max=round(ms[2] * 1e3, 2),
+                         block_sparsity=round(float(sk.mean()), 4), vload_sparsity=round(float(vsk.mean()), 4),
+                         bytes_per_launch=by, GBs=round(by / (ms[0] * 1e-3) / 1e9, 1),
+                         frac_of_hbm_peak=round(by / (ms[0] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         speedup_vs_dense_kernel=round(dense_ms[0] / ms[0], 4),
+                         bytes_ratio_dense_over_this=round(dense_bytes / by, 4)))
+    l0 = rows[0]["split_kernel_us"]
+    for r in rows:
+        r["speedup_vs_lambda0"] = round(l0 / r["split_kernel_us"], 4)
+    del x
+    torch.cuda.empty_cache()
+    return dict(workload=w.name, B=B, Hq=Hq, Hkv=w.Hkv, d=d, context=N, Bc=Bc, num_splits=S,
+                policy={"alpha": alpha, "beta": beta, "points": npts, "calibration_lengths": list(W.SWEEP_LENGTHS[:5])},
+                dense_kernel_us=round(dense_ms[0] * 1e3, 2), by_lambda=rows)
+
+
 def bench_mla(args, lib, torch, W):
     """MLA decode split kernel at 32K context, with 64- and 32-token blocks: time, HBM bytes (the cache
     rows are read once), the executed FLOPs (S for every head and token; P V for the kept blocks of each
@@ -581,7 +739,7 @@ def bench_mla(args, lib, torch, W):
             args_ = [(P(q), P(kv), P(o_part), P(lse_part), P(skip), B, Hq, N, dqk, dv, Bc,
                       ctypes.c_double(w.score_scale), ctypes.c_double(lam), S, ctypes.c_void_p(stream.cuda_stream))
                      for kv in kvs]
-            for i in range(4):
+            for i in range(20):  # warm-up (the first lambda's trials otherwise see the clocks ramp)
                 assert lib.blasst_decode_mla(*args_[i % 2]) == 0
             torch.cuda.synchronize()
             ts = []
@@ -705,6 +863,7 @@ def main():
             configs[name] = bench_config(name, args, lib, torch, W)
             torch.cuda.empty_cache()
         configs["ragged"] = bench_ragged(args, lib, torch, W)
+    sweep128 = None if args.no_length_sweep_timing else bench_decode_length_sweep(args, lib, torch, W, bsa)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args, d)
 
     by = d["bytes"]
@@ -738,15 +897,22 @@ def main():
                                               "min": round(min(d["split_trials_ms"]) * 1e3, 3),
                                               "median": round(d["split_ms"] * 1e3, 3),
                                               "max": round(max(d["split_trials_ms"]) * 1e3, 3)},
-                   "dense_step_us": round(d["dense_step_ms"] * 1e3, 3),
-                   "speedup_vs_lambda0": round(d["dense_step_ms"] / d["step_ms"], 4),
-                   "no_skip_step_us": round(d["ref_step_ms"] * 1e3, 3),
-                   "lambda0_speed_vs_no_skip": round(d["ref_step_ms"] / d["dense_step_ms"], 4),
+                   "lambda0_step_us": round(d["lambda0_step_ms"] * 1e3, 3),
+                   "speedup_vs_lambda0": round(d["lambda0_step_ms"] / d["step_ms"], 4),
+                   "dense_kernel_step_us": round(d["dense_step_ms"] * 1e3, 3),
+                   "dense_kernel_us": round(d["dense_kernel_ms"][0] * 1e3, 3),
+                   "load_ceiling_us": round(d["load_ceiling_ms"][0] * 1e3, 3),
+                   "load_ceiling_GBs_on_kv_bytes": round((by["k"] + by["v_dense"]) / (d["load_ceiling_ms"][0] * 1e-3)
+                                                          / 1e9, 1),
+                   "split_kernel_over_load_ceiling": round(d["split_ms"] / d["load_ceiling_ms"][0], 4),
+                   "speedup_vs_dense_kernel_step": round(d["dense_step_ms"] / d["step_ms"], 4),
+                   "lambda0_speed_vs_dense_kernel_step": round(d["dense_step_ms"] / d["lambda0_step_ms"], 4),
                    "block_sparsity": round(d["block_sparsity"], 5), "vload_sparsity": round(d["vload_sparsity"], 5),
-                   "bytes": by},
+                   "bytes": by, "lambda_sweep": d["lambda_sweep"]},
         "prefill": pre,
         "mla_decode": mla,
         "other_configs": configs,
+        "decode_length_sweep_128k": sweep128,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

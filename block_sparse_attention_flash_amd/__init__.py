@@ -21,7 +21,7 @@ import torch
 
 __all__ = ["blasst_prefill", "blasst_decode", "blasst_decode_combine", "blasst_prefill_margins",
            "blasst_decode_margins", "blasst_prefill_ragged", "blasst_decode_ragged", "blasst_decode_mla", "blasst_prefill_dense",
-           "blasst_decode_dense", "status_string",
+           "blasst_decode_dense", "blasst_decode_load_ceiling", "status_string",
            "prefill", "decode", "decode_combine", "prefill_margins", "decode_margins", "prefill_ragged",
            "decode_ragged", "decode_mla",
            "BlasstError", "library_path", "build"]
@@ -77,6 +77,8 @@ def _load():
         lib.blasst_prefill_dense.restype = i
         lib.blasst_decode_dense.argtypes = [P, P, P, P, P, i, i, i, i, i, i, i, P]
         lib.blasst_decode_dense.restype = i
+        lib.blasst_decode_load_ceiling.argtypes = [P, P, i, i, i, i, i, i, P]
+        lib.blasst_decode_load_ceiling.restype = i
         lib.blasst_status_string.argtypes = [i]
         lib.blasst_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -208,6 +210,18 @@ def blasst_decode_dense(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o_par
     st = _load().blasst_decode_dense(_ptr(q), _ptr(k), _ptr(v), _ptr(o_part), _ptr(lse_part), B, Hq, N, d,
                                      Hq // Hkv, Bc, num_splits, _stream(stream))
     _check("blasst_decode_dense", st)
+
+
+def blasst_decode_load_ceiling(k: torch.Tensor, v: torch.Tensor, Bc: int, num_splits: int,
+                               stream: Optional[torch.cuda.Stream] = None) -> None:
+    """Measurement only: the decode split kernel's HBM reads at lambda = 0, with nothing computed."""
+    _need(k, "k", torch.bfloat16)
+    _need(v, "v", torch.bfloat16)
+    if k.shape != v.shape or k.dim() != 4:
+        raise ValueError("k and v must be [B, Hkv, N, d] and of one shape")
+    B, Hkv, N, d = k.shape
+    st = _load().blasst_decode_load_ceiling(_ptr(k), _ptr(v), B, Hkv, N, d, Bc, num_splits, _stream(stream))
+    _check("blasst_decode_load_ceiling", st)
 
 
 def blasst_decode_ragged(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o_part: torch.Tensor,

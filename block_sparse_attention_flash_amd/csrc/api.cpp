@@ -74,7 +74,7 @@ blasst_status prefill_impl(const void* q, const void* k, const void* v, float* o
 blasst_status decode_impl(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
                           uint8_t* skip_mask, uint8_t* vskip_mask, const int32_t* seq_lens, int B, int Hq, int N,
                           int d, int gqa_ratio, int Bc, double lambda, int causal, int num_splits,
-                          blasst_stream_t stream) {
+                          blasst_stream_t stream, bool dense = false) {
     try {
         if (B < 0 || Hq < 0 || N <= 0 || d <= 0 || Bc <= 0 || gqa_ratio < 1) return BLASST_ERR_INVALID_ARG;
         if (Hq % gqa_ratio != 0 || !lambda_ok(lambda) || (causal != 0 && causal != 1))
@@ -82,7 +82,7 @@ blasst_status decode_impl(const void* q, const void* k, const void* v, float* o_
         const int64_t nk = ((int64_t)N + Bc - 1) / Bc;
         if (num_splits < 1 || num_splits > nk) return BLASST_ERR_INVALID_ARG;
         if (!supported_dim(d) || !supported_dim(Bc)) return BLASST_ERR_UNSUPPORTED;
-        if (gqa_ratio > 128) return BLASST_ERR_UNSUPPORTED;  // at most four 32-head workgroups per split
+        if (gqa_ratio > 128) return BLASST_ERR_UNSUPPORTED;  // at most two 64-head workgroups per split
         if ((int64_t)B * Hq == 0) return BLASST_OK;  // nothing to do; pointers are not read
         if (!q || !k || !v || !o_part || !lse_part) return BLASST_ERR_INVALID_ARG;
         if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o_part)) return BLASST_ERR_INVALID_ARG;
@@ -106,6 +106,8 @@ blasst_status decode_impl(const void* q, const void* k, const void* v, float* o_
         a.score_scale = static_cast<float>(kLog2e / std::sqrt((double)d));
         a.thr = log2_threshold(lambda);
         a.lens = seq_lens;
+        if (dense && gqa_ratio <= 32 && seq_lens == nullptr)
+            return from_hip(blasst::launch_decode_dense(a, d, Bc, reinterpret_cast<hipStream_t>(stream)));
         return from_hip(blasst::launch_decode(a, d, Bc, reinterpret_cast<hipStream_t>(stream)));
     } catch (...) {
         return BLASST_ERR_INTERNAL;
@@ -139,11 +141,34 @@ BLASST_EXPORT blasst_status blasst_prefill_dense(const void* q, const void* k, c
 BLASST_EXPORT blasst_status blasst_decode_dense(const void* q, const void* k, const void* v, float* o_part,
                                                 float* lse_part, int B, int Hq, int N, int d, int gqa_ratio, int Bc,
                                                 int num_splits, blasst_stream_t stream) {
-    // The decode test is one compare per (head, block) inside a batched decision; building
-    // it out changes only register allocation, so the reference runs the same kernel with
-    // the threshold at -inf (the compare never fires) and writes no decision bytes.
+    // Up to 32 heads per kv group: the single-pass dense kernel (K and V of each unit copied
+    // together, no decision).  Wider groups run the skip kernel with the threshold at -inf
+    // (the compare never fires) and no decision bytes.
     return decode_impl(q, k, v, o_part, lse_part, nullptr, nullptr, nullptr, B, Hq, N, d, gqa_ratio, Bc, 0.0, 1,
-                       num_splits, stream);
+                       num_splits, stream, true);
+}
+
+BLASST_EXPORT blasst_status blasst_decode_load_ceiling(const void* k, const void* v, int B, int Hkv, int N, int d,
+                                                       int Bc, int num_splits, blasst_stream_t stream) {
+    try {
+        if (B < 0 || Hkv < 0 || N <= 0 || d <= 0 || Bc <= 0) return BLASST_ERR_INVALID_ARG;
+        const int64_t nk = ((int64_t)N + Bc - 1) / Bc;
+        if (num_splits < 1 || num_splits > nk) return BLASST_ERR_INVALID_ARG;
+        if (!supported_dim(d) || !supported_dim(Bc)) return BLASST_ERR_UNSUPPORTED;
+        if ((int64_t)B * Hkv == 0) return BLASST_OK;
+        if (!k || !v || !aligned16(k) || !aligned16(v)) return BLASST_ERR_INVALID_ARG;
+        blasst::DecodeArgs a{};
+        a.k = static_cast<const uint16_t*>(k);
+        a.v = static_cast<const uint16_t*>(v);
+        a.B = B;
+        a.Hkv = Hkv;
+        a.N = N;
+        a.nk = (int)nk;
+        a.S = num_splits;
+        return from_hip(blasst::launch_decode_load_only(a, d, Bc, reinterpret_cast<hipStream_t>(stream)));
+    } catch (...) {
+        return BLASST_ERR_INTERNAL;
+    }
 }
 
 BLASST_EXPORT blasst_status blasst_decode(const void* q, const void* k, const void* v, float* o_part,

@@ -530,6 +530,300 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
     }
 }
 
+// s_waitcnt vmcnt(F * n) for a wave-uniform n in 0..7
+template <int F>
+__device__ __forceinline__ void wait_vm8(int n) {
+    switch (n) {
+        case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+        case 1: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(F) : "memory"); break;
+        case 2: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * F) : "memory"); break;
+        case 3: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * F) : "memory"); break;
+        case 4: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * F) : "memory"); break;
+        case 5: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(5 * F) : "memory"); break;
+        case 6: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(6 * F) : "memory"); break;
+        default: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(7 * F) : "memory"); break;
+    }
+}
+
+// Dense split-KV decode (FlashDecoding): the reference every skip is measured
+// against.  No decision, so nothing ties the waves together until the end: K
+// and V of each 32-key unit are copied HBM -> LDS together, one after the
+// other, through NSLOT (K, V) slot pairs per wave (a pair is read into
+// registers as soon as it lands and refilled at once), and each wave runs its
+// own online softmax (Eqs. 1-4 of the BLASST blog's section on FlashAttention,
+// with no Eq. 5) over its units w, w + W, w + 2W, ... of the split.  The waves'
+// (m, l, O) are merged by their maxima at the end.  DSPLIT = 2: two workgroups
+// per split, 8 apart in a 1-D grid (one XCD), both forming S from all of K and
+// each O for half of the d columns from half of every V row -- the layout of
+// decode_split_kernel's pairs.  The copies, swizzles and MFMA layouts are those
+// of decode_split_kernel: S^T = K q^T on MFMA 16x16x32 (keys x heads), then
+// O^T += V^T P^T with V^T read back transposed (ds_read_b64_tr_b16).  Up to 32
+// heads per kv group (NT <= 2).
+template <int D, int BC, int NT, int W, int NSLOT, int DSPLIT>
+__global__ __launch_bounds__(64 * W) void decode_dense_kernel(DecodeArgs a) {
+    constexpr int DS = D / 32;            // MFMA k-steps over d for S
+    constexpr int FR = D / 16;            // 16-byte copies per lane per 32-row K slice
+    constexpr int CPR = D / 8;            // 16-byte chunks per K row
+    constexpr int DV = D / DSPLIT;        // V columns this workgroup forms O for
+    constexpr int DTV = DV / 16;          // 16-wide d tiles of O^T
+    constexpr int FRV = DV / 16;          // 16-byte copies per lane per 32-row V slice
+    constexpr int CPRV = DV / 8;          // 16-byte chunks per staged V row
+    constexpr int HT = 16 * NT;           // head columns per workgroup
+    constexpr int KSLOT = 32 * D * 2;     // bytes of one 32-row K slice
+    constexpr int VSLOT = 32 * DV * 2;    // bytes of one 32-row V slice (half rows with DSPLIT = 2)
+    constexpr int PAIR = KSLOT + VSLOT;
+    static_assert(NT == 1 || NT == 2, "up to 32 heads");
+    static_assert(DSPLIT == 1 || DSPLIT == 2, "one or two workgroups per split");
+    static_assert(W * DTV * 4 * 64 * 4 <= NSLOT * W * PAIR, "O reduction must fit the staging area");
+    static_assert((FR + FRV) * (NSLOT - 1) <= 63, "wait counts fit vmcnt");
+
+    __shared__ __attribute__((aligned(16))) char lds_kv[NSLOT * W * PAIR];
+    __shared__ float lds_m[W][HT];
+    __shared__ float lds_l[W][64];
+
+    int split = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z, half = 0;
+    if constexpr (DSPLIT == 2) {
+        // workgroups L and L + 8 form a unit's two halves (workgroups go round-robin over 8 XCDs)
+        const int L = blockIdx.x;
+        const int unit = (L / 16) * 8 + (L % 8);
+        half = (L / 8) % 2;
+        if (unit >= a.S * a.Hkv * a.B) return;
+        split = unit % a.S;
+        hkv = (unit / a.S) % a.Hkv;
+        b = unit / (a.S * a.Hkv);
+    }
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int g = lane >> 4, n = lane & 15;
+    const int G = a.G, N = a.N;
+    const int j0 = (int)((int64_t)split * a.nk / a.S);
+    const int j1 = (int)((int64_t)(split + 1) * a.nk / a.S);
+    // 32-key units of the split that hold at least one key; this wave's share
+    const int nunits = max(0, min((j1 - j0) * (BC / 32), (N - j0 * BC + 31) / 32));
+    const int nu = nunits > wave ? (nunits - wave + W - 1) / W : 0;
+    const int key_base = j0 * BC;
+
+    const uint16_t* kbase = a.k + ((size_t)b * a.Hkv + hkv) * (size_t)N * D;
+    const uint16_t* vbase = a.v + ((size_t)b * a.Hkv + hkv) * (size_t)N * D + half * DV;
+
+    // q^T as the B operand: lane (g, n) holds q[head n][32s + 8g .. +8]
+    bf16x8 qf[NT][DS];
+    bool head_ok[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int h = nt * 16 + n;
+        head_ok[nt] = h < G;
+        const uint16_t* qrow = a.q + ((size_t)b * a.Hq + (size_t)hkv * G + (head_ok[nt] ? h : 0)) * D;
+#pragma unroll
+        for (int s = 0; s < DS; ++s) {
+            u32x4 z = {0u, 0u, 0u, 0u};
+            qf[nt][s] = as_bf16x8(head_ok[nt] ? load16(qrow + 32 * s + 8 * g) : z);
+        }
+    }
+
+    // unit u of this wave: keys key_base + 32 (wave + W u) ..; slot pair u % NSLOT
+    auto pair_of = [&](int u) { return lds_kv + (NSLOT * wave + u % NSLOT) * PAIR; };
+    auto issue = [&](int u) {
+        const int key0 = key_base + 32 * (wave + W * u);
+        const char* slot = pair_of(u);
+#pragma unroll
+        for (int f = 0; f < FR; ++f) {
+            const int p = 64 * f + lane;
+            const int row = p / CPR, cc = (p % CPR) ^ (row & (CPR - 1));
+            const int key = min(key0 + row, N - 1);
+            global_to_lds16(kbase + (size_t)key * D + cc * 8, lds_addr(slot + 1024 * f));
+        }
+#pragma unroll
+        for (int f = 0; f < FRV; ++f) {
+            const int p = 64 * f + lane;
+            const int row = p / CPRV, cc = (p % CPRV) ^ (row & (CPRV - 1));
+            const int key = min(key0 + row, N - 1);
+            global_to_lds16(vbase + (size_t)key * D + cc * 8, lds_addr(slot + KSLOT + 1024 * f));
+        }
+    };
+    for (int u = 0; u < min(NSLOT, nu); ++u) issue(u);
+
+    f32x4 oacc[NT][DTV];
+    float m_w[NT], l_part[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        m_w[nt] = kNegInf;
+        l_part[nt] = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < DTV; ++dt) oacc[nt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    for (int u = 0; u < nu; ++u) {
+        const int later = min(NSLOT - 1, nu - 1 - u);  // units issued after this one
+        const int key0 = key_base + 32 * (wave + W * u);
+        // K(u) and V(u) have landed once only the later units' copies are outstanding;
+        // both slices are read into registers at once, so the slot pair is refilled
+        // before any arithmetic on this unit
+        wait_vm8<FR + FRV>(later);
+        const char* kslot = pair_of(u);
+        const lds_char* vslot = (const lds_char*)(kslot + KSLOT);
+        u32x4 kf[2][DS];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int s = 0; s < DS; ++s) {
+                const int r = 16 * kt + n, c = 4 * s + g;
+                kf[kt][s] = *(const u32x4*)(kslot + r * (2 * D) + ((c ^ (r & (CPR - 1))) << 4));
+            }
+        bf16x8 vf[DTV];
+#pragma unroll
+        for (int dt = 0; dt < DTV; ++dt) {
+            const int cc = 2 * dt + ((n & 3) >> 1);
+            const int r0 = 4 * g + (n >> 2), r1 = 16 + 4 * g + (n >> 2);
+            const u32x2 lo = lds_read_tr16(vslot + r0 * (2 * DV) + ((cc ^ (r0 & (CPRV - 1))) << 4) + (n & 1) * 8);
+            const u32x2 hi = lds_read_tr16(vslot + r1 * (2 * DV) + ((cc ^ (r1 & (CPRV - 1))) << 4) + (n & 1) * 8);
+            vf[dt] = as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y});
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the slot pair has been read
+        if (u + NSLOT < nu) issue(u + NSLOT);
+
+        bf16x8 pf[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            f32x4 t[2];
+            float um = kNegInf;
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < DS; ++s) acc = mfma16x16x32(as_bf16x8(kf[kt][s]), qf[nt][s], acc);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int key = key0 + 16 * kt + 4 * g + i;
+                    float x = acc[i] * a.score_scale;
+                    x = key < N ? x : kNegInf;
+                    acc[i] = x;
+                    um = fmaxf(um, x);
+                }
+                t[kt] = acc;
+            }
+            um = wave_max_xor32(wave_max_xor16(um));  // over the unit's 32 keys (every unit holds one)
+            const float m_new = fmaxf(m_w[nt], um);
+            const float alpha = exp2_fast(m_w[nt] - m_new);  // 0 on the first unit
+            m_w[nt] = m_new;
+            if (!__all(alpha == 1.f)) {
+                l_part[nt] *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < DTV; ++dt) oacc[nt][dt] *= alpha;
+            }
+            float p[8];
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) p[4 * kt + i] = exp2_fast(t[kt][i] - m_new);
+            l_part[nt] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+            pf[nt] = as_bf16x8(u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                                     pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])});
+        }
+#pragma unroll
+        for (int dt = 0; dt < DTV; ++dt)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) oacc[nt][dt] = mfma16x16x32(vf[dt], pf[nt], oacc[nt][dt]);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+    // ---- merge the waves' (m, l, O) by their maxima; write the split's result
+    __syncthreads();
+    float* red = (float*)lds_kv;  // [W waves][DTV][4][64]
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        if (g == 0) lds_m[wave][nt * 16 + n] = m_w[nt];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        float M = kNegInf;
+#pragma unroll
+        for (int w = 0; w < W; ++w) M = fmaxf(M, lds_m[w][nt * 16 + n]);
+        // a wave with no unit has m = -inf and weight 0; a split with no key has M = -inf
+        const float sc = M == kNegInf ? 0.f : exp2_fast(m_w[nt] - M);
+        const float l = wave_sum_xor32(wave_sum_xor16(l_part[nt])) * sc;
+#pragma unroll
+        for (int dt = 0; dt < DTV; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) red[((wave * DTV + dt) * 4 + i) * 64 + lane] = oacc[nt][dt][i] * sc;
+        lds_l[wave][lane] = l;
+        __syncthreads();
+        float lt = 0.f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) lt += lds_l[w][lane];
+        const int h = nt * 16 + n;
+        if (h < G) {
+            const size_t orow = ((size_t)b * a.Hq + (size_t)hkv * G + h) * a.S + split;
+            const float inv = lt > 0.f ? 1.f / lt : 0.f;  // 0: a split with no key
+            for (int dt = wave; dt < DTV; dt += W) {
+                float o4[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float x = 0.f;
+#pragma unroll
+                    for (int w = 0; w < W; ++w) x += red[((w * DTV + dt) * 4 + i) * 64 + lane];
+                    o4[i] = x * inv;
+                }
+                *(f32x4*)(a.o_part + orow * D + half * DV + 16 * dt + 4 * g) = f32x4{o4[0], o4[1], o4[2], o4[3]};
+            }
+            if (wave == 0 && g == 0 && half == 0) a.lse_part[orow] = lt > 0.f ? M * kLn2 + logf(lt) : kNegInf;
+        }
+        __syncthreads();
+    }
+}
+
+// The split kernel's loads alone: a measurement kernel, not part of any result.
+// It issues the HBM -> LDS copies decode_split_kernel issues for two workgroups
+// per split at lambda = 0 -- every 32-key K unit of the split by both
+// workgroups of the pair, then each workgroup half of every V row -- through
+// the same rings (eight waves, two 8 KiB slots each), with no arithmetic and
+// no barrier.  Its time is the floor those bytes and that access pattern set
+// for the decode kernel on this part.
+template <int D, int BC>
+__global__ __launch_bounds__(512) void decode_load_only_kernel(DecodeArgs a) {
+    constexpr int W = 8, NSLOT = 2;
+    constexpr int FR = D / 16, CPR = D / 8;
+    constexpr int DV = D / 2, FRV = DV / 16, CPRV = DV / 8;
+    constexpr int SLOT = 32 * D * 2;
+    __shared__ __attribute__((aligned(16))) char lds[NSLOT * W * SLOT];
+    const int L = blockIdx.x;
+    const int unit = (L / 16) * 8 + (L % 8);
+    const int half = (L / 8) % 2;
+    if (unit >= a.S * a.Hkv * a.B) return;
+    const int split = unit % a.S, hkv = (unit / a.S) % a.Hkv, b = unit / (a.S * a.Hkv);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int N = a.N;
+    const int j0 = (int)((int64_t)split * a.nk / a.S), j1 = (int)((int64_t)(split + 1) * a.nk / a.S);
+    const int key_base = j0 * BC;
+    const int nunits = max(0, min((j1 - j0) * (BC / 32), (N - key_base + 31) / 32));
+    const uint16_t* kbase = a.k + ((size_t)b * a.Hkv + hkv) * (size_t)N * D;
+    const uint16_t* vbase = a.v + ((size_t)b * a.Hkv + hkv) * (size_t)N * D + half * DV;
+    int i = 0;
+    for (int U = wave; U < nunits; U += W, ++i) {
+        if (i >= NSLOT) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(FR) : "memory");
+        const char* slot = lds + (NSLOT * wave + (i % NSLOT)) * SLOT;
+#pragma unroll
+        for (int f = 0; f < FR; ++f) {
+            const int p = 64 * f + lane, row = p / CPR, cc = (p % CPR) ^ (row & (CPR - 1));
+            const int key = min(key_base + 32 * U + row, N - 1);
+            global_to_lds16(kbase + (size_t)key * D + cc * 8, lds_addr(slot + 1024 * f));
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    i = 0;
+    for (int U = wave; U < nunits; U += W, ++i) {
+        if (i >= 2 * NSLOT) asm volatile("s_waitcnt vmcnt(%0)" ::"n"((2 * NSLOT - 1) * FRV) : "memory");
+        const char* slot = lds + NSLOT * wave * SLOT + (i % (2 * NSLOT)) * (SLOT / 2);
+#pragma unroll
+        for (int f = 0; f < FRV; ++f) {
+            const int p = 64 * f + lane, row = p / CPRV, cc = (p % CPRV) ^ (row & (CPRV - 1));
+            const int key = min(key_base + 32 * U + row, N - 1);
+            global_to_lds16(vbase + (size_t)key * D + cc * 8, lds_addr(slot + 1024 * f));
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 // Merge of S split results per (b, head) row.  One workgroup per row, one
 // thread per d column.  Up to 32 splits every load is issued at once (one
 // memory round trip); beyond that the splits are walked in a loop.
@@ -718,6 +1012,45 @@ hipError_t launch_split_nt(const DecodeArgs& a, hipStream_t stream) {
 hipError_t launch_decode(const DecodeArgs& a, int d, int Bc, hipStream_t stream) {
     if (d == 128) return Bc == 128 ? launch_split_nt<128, 128>(a, stream) : launch_split_nt<128, 64>(a, stream);
     return Bc == 128 ? launch_split_nt<64, 128>(a, stream) : launch_split_nt<64, 64>(a, stream);
+}
+
+namespace {
+template <int D, int BC, int NT>
+hipError_t launch_dense_shape(const DecodeArgs& a, hipStream_t stream) {
+    // eight waves, one (K, V) slot pair each (two at d = 64): 128 KiB in flight per workgroup;
+    // at most 128 (b, kv head, split) units: two workgroups per split, each half of V's columns
+    constexpr int NSLOT = D == 128 ? 1 : 2;
+    const int64_t units = (int64_t)a.S * a.Hkv * a.B;
+    if (units <= 128) {
+        const dim3 grid((unsigned)(2 * ((units + 7) / 8) * 8));
+        hipLaunchKernelGGL((decode_dense_kernel<D, BC, NT, 8, NSLOT, 2>), grid, dim3(512), 0, stream, a);
+    } else {
+        hipLaunchKernelGGL((decode_dense_kernel<D, BC, NT, 8, NSLOT, 1>), dim3(a.S, a.Hkv, a.B), dim3(512), 0, stream, a);
+    }
+    return hipGetLastError();
+}
+
+template <int D, int BC>
+hipError_t launch_dense_nt(const DecodeArgs& a, hipStream_t stream) {
+    return a.G <= 16 ? launch_dense_shape<D, BC, 1>(a, stream) : launch_dense_shape<D, BC, 2>(a, stream);
+}
+}  // namespace
+
+hipError_t launch_decode_dense(const DecodeArgs& a, int d, int Bc, hipStream_t stream) {
+    if (a.G > 32 || a.lens != nullptr) return hipErrorInvalidValue;
+    if (d == 128) return Bc == 128 ? launch_dense_nt<128, 128>(a, stream) : launch_dense_nt<128, 64>(a, stream);
+    return Bc == 128 ? launch_dense_nt<64, 128>(a, stream) : launch_dense_nt<64, 64>(a, stream);
+}
+
+hipError_t launch_decode_load_only(const DecodeArgs& a, int d, int Bc, hipStream_t stream) {
+    const int64_t units = (int64_t)a.S * a.Hkv * a.B;
+    if (units > (int64_t)INT_MAX / 16) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)(2 * ((units + 7) / 8) * 8));
+    if (d == 128 && Bc == 128) hipLaunchKernelGGL((decode_load_only_kernel<128, 128>), grid, dim3(512), 0, stream, a);
+    else if (d == 128) hipLaunchKernelGGL((decode_load_only_kernel<128, 64>), grid, dim3(512), 0, stream, a);
+    else if (Bc == 128) hipLaunchKernelGGL((decode_load_only_kernel<64, 128>), grid, dim3(512), 0, stream, a);
+    else hipLaunchKernelGGL((decode_load_only_kernel<64, 64>), grid, dim3(512), 0, stream, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_decode_margins(const DecodeArgs& a, int d, int Bc, hipStream_t stream) {

@@ -52,6 +52,10 @@ struct MlaArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs& a, int d, int Bc, hipStream_t stream);
+// Dense split-KV decode, K and V streamed together (no skip test); G <= 32, plain batches.
+hipError_t launch_decode_dense(const DecodeArgs& a, int d, int Bc, hipStream_t stream);
+// Measurement only: the loads of the split kernel's two-workgroups-per-split layout at lambda = 0, nothing else.
+hipError_t launch_decode_load_only(const DecodeArgs& a, int d, int Bc, hipStream_t stream);
 hipError_t launch_decode_mla(const MlaArgs& a, int Bc, hipStream_t stream);
 hipError_t launch_decode_combine(const float* o_part, const float* lse_part, float* o, float* lse, int rows,
                                  int d, int S, hipStream_t stream);

@@ -111,14 +111,24 @@ blasst_status blasst_decode(const void* q, const void* k, const void* v, float* 
                             int causal, int num_splits, blasst_stream_t stream);
 
 /*
- * Dense references: blasst_prefill built without the skip test (no row votes,
- * no vote exchange between waves, every tile kept), and blasst_decode with no
- * block ever skipped (its test, one compare per head and block inside the
- * batched decision, runs with the threshold at -inf) -- both without decision
- * bytes.  Same arguments minus lambda and the masks; results equal the
- * lambda = 0 calls.  They exist to measure what the test costs when nothing is
- * skipped (the blog's 0.96-1.00x at 0% sparsity, section on the decision
- * cost), and serve callers that want plain attention.
+ * Dense references (plain softmax attention, nothing ever skipped, no decision
+ * bytes; same arguments minus lambda and the masks; results equal the
+ * lambda = 0 calls up to rounding order).  They are what the blog measures its
+ * kernels against (dense FlashAttention; sections on kernel speed and on the
+ * decision cost, 0.96-1.00x at 0% sparsity), and serve callers that want
+ * plain attention.
+ *
+ * blasst_prefill_dense: blasst_prefill built without the skip test (no row
+ * votes, no vote exchange between waves, every tile kept).
+ *
+ * blasst_decode_dense: split-KV decode in one pass (FlashDecoding).  For
+ * gqa_ratio <= 32 a kernel of its own copies K and V of every 32-key unit
+ * together and runs an online softmax per wave, with no decision and no
+ * barrier before the merge of the waves -- the dense decode the skip kernel's
+ * V savings are measured against.  Wider groups run blasst_decode's kernel
+ * with the threshold at -inf.  o_part and lse_part are as blasst_decode's, so
+ * blasst_decode_combine merges them; num_splits is the caller's choice (a
+ * dense decode picks the split count that fills the GPU).
  * Errors as blasst_prefill / blasst_decode.
  */
 blasst_status blasst_prefill_dense(const void* q, const void* k, const void* v, float* o, float* lse,
@@ -127,6 +137,22 @@ blasst_status blasst_prefill_dense(const void* q, const void* k, const void* v, 
 blasst_status blasst_decode_dense(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
                                   int B, int Hq, int N, int d, int gqa_ratio, int Bc, int num_splits,
                                   blasst_stream_t stream);
+
+/*
+ * blasst_decode_load_ceiling -- a measurement call, not part of any result.
+ * Issues exactly the HBM reads blasst_decode's kernel issues at lambda = 0 in
+ * its two-workgroups-per-split layout (every K row of a split read by both
+ * workgroups of the pair, which share one L2; each workgroup then half of
+ * every V row), through the same LDS rings, and nothing else: no arithmetic,
+ * no barrier, no output.  Its time is the floor that the bytes of
+ * K + V = 2 * B * Hkv * N * d * 2 and that access pattern set for the decode
+ * split kernel (the memory-bound decode kernel of the BLASST blog's section
+ * on the decode kernel), so a bench can state how far the kernel is from its
+ * own data movement.  k, v as blasst_decode; same validation (d, Bc in
+ * {64, 128}, 1 <= num_splits <= ceil(N / Bc)).  Asynchronous on stream.
+ */
+blasst_status blasst_decode_load_ceiling(const void* k, const void* v, int B, int Hkv, int N, int d, int Bc,
+                                         int num_splits, blasst_stream_t stream);
 
 /*
  * Ragged batches: one length per sequence (the serving-shaped form of the same

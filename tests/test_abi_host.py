@@ -27,8 +27,9 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert declared() == ["blasst_decode", "blasst_decode_combine", "blasst_decode_dense", "blasst_decode_margins",
-                          "blasst_decode_mla", "blasst_decode_ragged", "blasst_prefill", "blasst_prefill_dense",
+    assert declared() == ["blasst_decode", "blasst_decode_combine", "blasst_decode_dense",
+                          "blasst_decode_load_ceiling", "blasst_decode_margins", "blasst_decode_mla",
+                          "blasst_decode_ragged", "blasst_prefill", "blasst_prefill_dense",
                           "blasst_prefill_margins", "blasst_prefill_ragged", "blasst_status_string"]
 
 
@@ -185,3 +186,13 @@ def test_dense_references_validate_like_the_plain_calls(lib):
     assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4, 256, 128, 4, 128, 3, None) == 1   # 3 splits > 2 blocks
     assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4, 256, 128, 4, 256, 1, None) == 2
     assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 4, 256, 128, 4, 128, 1, None) == 0
+
+
+def test_load_ceiling_validates_like_decode(lib):
+    f = lib.blasst_decode_load_ceiling
+    f.argtypes = [P, P, I, I, I, I, I, I, P]
+    assert f(FAKE, FAKE, 1, 8, 256, 128, 128, 3, None) == 1     # 3 splits > 2 blocks
+    assert f(FAKE, FAKE, 1, 8, 256, 96, 128, 1, None) == 2      # d = 96
+    assert f(None, FAKE, 1, 8, 256, 128, 128, 1, None) == 1     # null k
+    assert f(P(0x1008), FAKE, 1, 8, 256, 128, 128, 1, None) == 1  # misaligned k
+    assert f(FAKE, FAKE, 0, 8, 256, 128, 128, 1, None) == 0     # empty batch: nothing launched
