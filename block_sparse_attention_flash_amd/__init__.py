@@ -21,7 +21,8 @@ import torch
 
 __all__ = ["blasst_prefill", "blasst_decode", "blasst_decode_combine", "blasst_prefill_margins",
            "blasst_decode_margins", "blasst_prefill_ragged", "blasst_decode_ragged", "blasst_decode_mla", "blasst_prefill_dense",
-           "blasst_decode_dense", "blasst_decode_load_ceiling", "status_string",
+           "blasst_decode_dense", "blasst_decode_load_ceiling", "blasst_decode_step", "decode_step_workspace_size",
+           "decode_step", "status_string",
            "prefill", "decode", "decode_combine", "prefill_margins", "decode_margins", "prefill_ragged",
            "decode_ragged", "decode_mla",
            "BlasstError", "library_path", "build"]
@@ -77,6 +78,10 @@ def _load():
         lib.blasst_prefill_dense.restype = i
         lib.blasst_decode_dense.argtypes = [P, P, P, P, P, i, i, i, i, i, i, i, P]
         lib.blasst_decode_dense.restype = i
+        lib.blasst_decode_step.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_size_t, i, i, i, i, i, i, d, i, i, P]
+        lib.blasst_decode_step.restype = i
+        lib.blasst_decode_step_workspace_size.argtypes = [i, i, i, i]
+        lib.blasst_decode_step_workspace_size.restype = ctypes.c_size_t
         lib.blasst_decode_load_ceiling.argtypes = [P, P, i, i, i, i, i, i, P]
         lib.blasst_decode_load_ceiling.restype = i
         lib.blasst_status_string.argtypes = [i]
@@ -210,6 +215,52 @@ def blasst_decode_dense(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o_par
     st = _load().blasst_decode_dense(_ptr(q), _ptr(k), _ptr(v), _ptr(o_part), _ptr(lse_part), B, Hq, N, d,
                                      Hq // Hkv, Bc, num_splits, _stream(stream))
     _check("blasst_decode_dense", st)
+
+
+def decode_step_workspace_size(B: int, Hq: int, d: int, num_splits: int) -> int:
+    """Bytes of the split partials blasst_decode_step needs."""
+    return int(_load().blasst_decode_step_workspace_size(B, Hq, d, num_splits))
+
+
+def blasst_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: Optional[torch.Tensor],
+                       skip_mask: Optional[torch.Tensor], vskip_mask: Optional[torch.Tensor], workspace: torch.Tensor,
+                       Bc: int, lam: float, num_splits: int, stream: Optional[torch.cuda.Stream] = None) -> None:
+    """One decode step (split kernel + merge) with the partials in `workspace` (uint8 on the GPU)."""
+    B, Hq, one, d = q.shape
+    Hkv, N = k.shape[1], k.shape[2]
+    _need(q, "q", torch.bfloat16)
+    _need(k, "k", torch.bfloat16)
+    _need(v, "v", torch.bfloat16)
+    _need(o, "o", torch.float32)
+    _need(workspace, "workspace", torch.uint8)
+    if one != 1 or v.shape != k.shape or o.shape != (B, Hq, d) or (lse is not None and lse.shape != (B, Hq)):
+        raise ValueError("q [B,Hq,1,d], k and v [B,Hkv,N,d], o [B,Hq,d], lse [B,Hq]")
+    if lse is not None:
+        _need(lse, "lse", torch.float32)
+    nk = -(-N // Bc)
+    for t, shp, nm in ((skip_mask, (B, Hq, nk), "skip_mask"), (vskip_mask, (B, Hkv, nk), "vskip_mask")):
+        if t is not None:
+            _need(t, nm, torch.uint8)
+            if t.shape != shp:
+                raise ValueError("%s must be %s" % (nm, shp))
+    st = _load().blasst_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(skip_mask), _ptr(vskip_mask),
+                                    _ptr(workspace), workspace.numel(), B, Hq, N, d, Hq // Hkv, Bc, float(lam), 1,
+                                    num_splits, _stream(stream))
+    _check("blasst_decode_step", st)
+
+
+def decode_step(q, k, v, lam: float, num_splits: int, Bc: int = 128, with_masks: bool = True):
+    """Allocating wrapper: returns (o [B,Hq,d], lse [B,Hq], skip or None, vskip or None)."""
+    B, Hq, _, d = q.shape
+    Hkv, N = k.shape[1], k.shape[2]
+    nk = -(-N // Bc)
+    o = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    skip = torch.empty((B, Hq, nk), dtype=torch.uint8, device=q.device) if with_masks else None
+    vskip = torch.empty((B, Hkv, nk), dtype=torch.uint8, device=q.device) if with_masks else None
+    ws = torch.empty(max(16, decode_step_workspace_size(B, Hq, d, num_splits)), dtype=torch.uint8, device=q.device)
+    blasst_decode_step(q, k, v, o, lse, skip, vskip, ws, Bc, lam, num_splits)
+    return o, lse, skip, vskip
 
 
 def blasst_decode_load_ceiling(k: torch.Tensor, v: torch.Tensor, Bc: int, num_splits: int,

@@ -188,6 +188,62 @@ BLASST_EXPORT blasst_status blasst_decode_ragged(const void* q, const void* k, c
                        lambda, 1, num_splits, stream);
 }
 
+namespace {
+
+// Bytes of the split partials of one decode step: o_part [B,Hq,S,d] then lse_part [B,Hq,S] (fp32).
+size_t step_workspace_bytes(int B, int Hq, int d, int num_splits) {
+    return (size_t)B * Hq * num_splits * ((size_t)d + 1) * sizeof(float);
+}
+
+// blasst_decode into the partials at `ws`, then the merge into o / lse.
+blasst_status decode_step_impl(const void* q, const void* k, const void* v, float* o, float* lse, uint8_t* skip_mask,
+                               uint8_t* vskip_mask, void* ws, int B, int Hq, int N, int d, int gqa_ratio, int Bc,
+                               double lambda, int causal, int num_splits, blasst_stream_t stream) {
+    float* o_part = static_cast<float*>(ws);
+    float* lse_part = o_part + (size_t)B * Hq * num_splits * d;
+    blasst_status st = decode_impl(q, k, v, o_part, lse_part, skip_mask, vskip_mask, nullptr, B, Hq, N, d, gqa_ratio,
+                                   Bc, lambda, causal, num_splits, stream);
+    if (st != BLASST_OK) return st;
+    try {
+        return from_hip(blasst::launch_decode_combine(o_part, lse_part, o, lse, B * Hq, d, num_splits,
+                                                      reinterpret_cast<hipStream_t>(stream)));
+    } catch (...) {
+        return BLASST_ERR_INTERNAL;
+    }
+}
+
+// Arguments of a decode step that blasst_decode does not check: the output and its size.
+blasst_status step_args_ok(float* o, int B, int Hq, int d, int num_splits) {
+    if (B < 0 || Hq < 0 || d <= 0 || num_splits < 1) return BLASST_ERR_INVALID_ARG;
+    if ((int64_t)B * Hq == 0) return BLASST_OK;
+    if (!o) return BLASST_ERR_INVALID_ARG;
+    if ((int64_t)B * Hq > INT32_MAX) return BLASST_ERR_UNSUPPORTED;
+    return BLASST_OK;
+}
+
+}  // namespace
+
+BLASST_EXPORT size_t blasst_decode_step_workspace_size(int B, int Hq, int d, int num_splits) {
+    if (B < 0 || Hq < 0 || d <= 0 || num_splits < 1) return 0;
+    return step_workspace_bytes(B, Hq, d, num_splits);
+}
+
+BLASST_EXPORT blasst_status blasst_decode_step(const void* q, const void* k, const void* v, float* o, float* lse,
+                                               uint8_t* skip_mask, uint8_t* vskip_mask, void* workspace,
+                                               size_t workspace_bytes, int B, int Hq, int N, int d, int gqa_ratio,
+                                               int Bc, double lambda, int causal, int num_splits,
+                                               blasst_stream_t stream) {
+    blasst_status st = step_args_ok(o, B, Hq, d, num_splits);
+    if (st != BLASST_OK || (int64_t)B * Hq == 0)
+        return st != BLASST_OK ? st
+                               : decode_impl(q, k, v, nullptr, nullptr, skip_mask, vskip_mask, nullptr, B, Hq, N, d,
+                                             gqa_ratio, Bc, lambda, causal, num_splits, stream);
+    if (!workspace || !aligned16(workspace) || workspace_bytes < step_workspace_bytes(B, Hq, d, num_splits))
+        return BLASST_ERR_INVALID_ARG;
+    return decode_step_impl(q, k, v, o, lse, skip_mask, vskip_mask, workspace, B, Hq, N, d, gqa_ratio, Bc, lambda,
+                            causal, num_splits, stream);
+}
+
 BLASST_EXPORT blasst_status blasst_decode_combine(const float* o_part, const float* lse_part, float* o, float* lse,
                                                   int B, int Hq, int d, int num_splits, blasst_stream_t stream) {
     try {

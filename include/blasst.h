@@ -39,6 +39,7 @@
 #ifndef BLASST_H
 #define BLASST_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -137,6 +138,28 @@ blasst_status blasst_prefill_dense(const void* q, const void* k, const void* v, 
 blasst_status blasst_decode_dense(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
                                   int B, int Hq, int N, int d, int gqa_ratio, int Bc, int num_splits,
                                   blasst_stream_t stream);
+
+/*
+ * blasst_decode_step: one whole split-KV decode step in one call -- blasst_decode
+ * followed by blasst_decode_combine (the split-KV merge by log-sum-exp, SANTA
+ * notes, method details), for callers that want O and not the split partials.
+ * The partials live in a caller-provided workspace of
+ * blasst_decode_step_workspace_size(B, Hq, d, num_splits) =
+ * B*Hq*num_splits*(d+1)*4 bytes (o_part [B,Hq,S,d] fp32 then lse_part
+ * [B,Hq,S] fp32), 16-byte aligned, which the call overwrites and the caller
+ * owns; its contents after the call are unspecified.
+ *   o          fp32 [B, Hq, d]: the merged output (the query's attention row)
+ *   lse        fp32 [B, Hq] or NULL: the merged log-sum-exp
+ *   skip_mask, vskip_mask, and every other argument: as blasst_decode.
+ * Errors: as blasst_decode, plus INVALID_ARG for a NULL o, or a NULL,
+ * misaligned or too small workspace (when B*Hq != 0).  Asynchronous on stream.
+ * blasst_decode_step_workspace_size returns 0 for invalid sizes.
+ */
+size_t blasst_decode_step_workspace_size(int B, int Hq, int d, int num_splits);
+blasst_status blasst_decode_step(const void* q, const void* k, const void* v, float* o, float* lse,
+                                 uint8_t* skip_mask, uint8_t* vskip_mask, void* workspace, size_t workspace_bytes,
+                                 int B, int Hq, int N, int d, int gqa_ratio, int Bc, double lambda, int causal,
+                                 int num_splits, blasst_stream_t stream);
 
 /*
  * blasst_decode_load_ceiling -- a measurement call, not part of any result.

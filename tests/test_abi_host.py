@@ -29,8 +29,9 @@ def lib():
 def test_header_declares_the_entry_points():
     assert declared() == ["blasst_decode", "blasst_decode_combine", "blasst_decode_dense",
                           "blasst_decode_load_ceiling", "blasst_decode_margins", "blasst_decode_mla",
-                          "blasst_decode_ragged", "blasst_prefill", "blasst_prefill_dense",
-                          "blasst_prefill_margins", "blasst_prefill_ragged", "blasst_status_string"]
+                          "blasst_decode_ragged", "blasst_decode_step", "blasst_decode_step_workspace_size",
+                          "blasst_prefill", "blasst_prefill_dense", "blasst_prefill_margins", "blasst_prefill_ragged",
+                          "blasst_status_string"]
 
 
 def test_exports_match_header(lib):
@@ -196,3 +197,28 @@ def test_load_ceiling_validates_like_decode(lib):
     assert f(None, FAKE, 1, 8, 256, 128, 128, 1, None) == 1     # null k
     assert f(P(0x1008), FAKE, 1, 8, 256, 128, 128, 1, None) == 1  # misaligned k
     assert f(FAKE, FAKE, 0, 8, 256, 128, 128, 1, None) == 0     # empty batch: nothing launched
+
+
+def test_decode_step_validates_its_workspace(lib):
+    sz = lib.blasst_decode_step_workspace_size
+    sz.argtypes = [I, I, I, I]
+    sz.restype = ctypes.c_size_t
+    assert sz(1, 32, 128, 16) == 32 * 16 * 129 * 4
+    assert sz(1, 32, 128, 0) == 0 and sz(-1, 32, 128, 4) == 0
+    f = lib.blasst_decode_step
+    f.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_size_t, I, I, I, I, I, I, D, I, I, P]
+    need = 4 * 2 * 129 * 4
+    ok = (FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, need, 1, 4, 256, 128, 4, 128, 1e-3, 1, 2, None)
+
+    def call(**kw):
+        a = list(ok)
+        for k, v in kw.items():
+            a[{"o": 3, "ws": 7, "ws_bytes": 8, "B": 9, "S": 17, "lam": 15}[k]] = v
+        return f(*a)
+    assert call(ws=None) == 1
+    assert call(ws=P(0x1004)) == 1                # misaligned workspace
+    assert call(ws_bytes=need - 1) == 1           # too small
+    assert call(o=None) == 1
+    assert call(S=3, ws_bytes=10**6) == 1         # 3 splits > 2 blocks
+    assert call(lam=1.0) == 1
+    assert call(B=0, ws=None, o=None) == 0        # empty batch: validated, nothing launched
