@@ -74,7 +74,7 @@ blasst_status prefill_impl(const void* q, const void* k, const void* v, float* o
 blasst_status decode_impl(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
                           uint8_t* skip_mask, uint8_t* vskip_mask, const int32_t* seq_lens, int B, int Hq, int N,
                           int d, int gqa_ratio, int Bc, double lambda, int causal, int num_splits,
-                          blasst_stream_t stream, bool dense = false) {
+                          blasst_stream_t stream, bool dense = false, bool validate_only = false) {
     try {
         if (B < 0 || Hq < 0 || N <= 0 || d <= 0 || Bc <= 0 || gqa_ratio < 1) return BLASST_ERR_INVALID_ARG;
         if (Hq % gqa_ratio != 0 || !lambda_ok(lambda) || (causal != 0 && causal != 1))
@@ -84,9 +84,10 @@ blasst_status decode_impl(const void* q, const void* k, const void* v, float* o_
         if (!supported_dim(d) || !supported_dim(Bc)) return BLASST_ERR_UNSUPPORTED;
         if (gqa_ratio > 128) return BLASST_ERR_UNSUPPORTED;  // at most two 64-head workgroups per split
         if ((int64_t)B * Hq == 0) return BLASST_OK;  // nothing to do; pointers are not read
-        if (!q || !k || !v || !o_part || !lse_part) return BLASST_ERR_INVALID_ARG;
+        if (!q || !k || !v || (!validate_only && (!o_part || !lse_part))) return BLASST_ERR_INVALID_ARG;
         if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o_part)) return BLASST_ERR_INVALID_ARG;
         if (B > 65535 || Hq / gqa_ratio > 65535) return BLASST_ERR_UNSUPPORTED;
+        if (validate_only) return BLASST_OK;
 
         blasst::DecodeArgs a;
         a.q = static_cast<const uint16_t*>(q);
@@ -234,10 +235,10 @@ BLASST_EXPORT blasst_status blasst_decode_step(const void* q, const void* k, con
                                                int Bc, double lambda, int causal, int num_splits,
                                                blasst_stream_t stream) {
     blasst_status st = step_args_ok(o, B, Hq, d, num_splits);
-    if (st != BLASST_OK || (int64_t)B * Hq == 0)
-        return st != BLASST_OK ? st
-                               : decode_impl(q, k, v, nullptr, nullptr, skip_mask, vskip_mask, nullptr, B, Hq, N, d,
-                                             gqa_ratio, Bc, lambda, causal, num_splits, stream);
+    if (st == BLASST_OK)
+        st = decode_impl(q, k, v, nullptr, nullptr, skip_mask, vskip_mask, nullptr, B, Hq, N, d, gqa_ratio, Bc, lambda,
+                         causal, num_splits, stream, false, true);
+    if (st != BLASST_OK || (int64_t)B * Hq == 0) return st;
     if (!workspace || !aligned16(workspace) || workspace_bytes < step_workspace_bytes(B, Hq, d, num_splits))
         return BLASST_ERR_INVALID_ARG;
     return decode_step_impl(q, k, v, o, lse, skip_mask, vskip_mask, workspace, B, Hq, N, d, gqa_ratio, Bc, lambda,
