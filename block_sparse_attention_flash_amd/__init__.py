@@ -22,6 +22,7 @@ import torch
 __all__ = ["blasst_prefill", "blasst_decode", "blasst_decode_combine", "blasst_prefill_margins",
            "blasst_decode_margins", "blasst_prefill_ragged", "blasst_decode_ragged", "blasst_decode_mla", "blasst_prefill_dense",
            "blasst_decode_dense", "blasst_decode_load_ceiling", "blasst_decode_step", "decode_step_workspace_size",
+           "blasst_decode_step_noalloc",
            "decode_step", "status_string",
            "prefill", "decode", "decode_combine", "prefill_margins", "decode_margins", "prefill_ragged",
            "decode_ragged", "decode_mla",
@@ -80,6 +81,10 @@ def _load():
         lib.blasst_decode_dense.restype = i
         lib.blasst_decode_step.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_size_t, i, i, i, i, i, i, d, i, i, P]
         lib.blasst_decode_step.restype = i
+        lib.blasst_decode_step_noalloc.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, i, d, i, i, P]
+        lib.blasst_decode_step_noalloc.restype = i
+        lib.blasst_decode_step_noalloc_max_bytes.argtypes = []
+        lib.blasst_decode_step_noalloc_max_bytes.restype = ctypes.c_size_t
         lib.blasst_decode_step_workspace_size.argtypes = [i, i, i, i]
         lib.blasst_decode_step_workspace_size.restype = ctypes.c_size_t
         lib.blasst_decode_load_ceiling.argtypes = [P, P, i, i, i, i, i, i, P]
@@ -247,6 +252,37 @@ def blasst_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: tor
                                     _ptr(workspace), workspace.numel(), B, Hq, N, d, Hq // Hkv, Bc, float(lam), 1,
                                     num_splits, _stream(stream))
     _check("blasst_decode_step", st)
+
+
+def blasst_decode_step_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                               lse: Optional[torch.Tensor], skip_mask: Optional[torch.Tensor],
+                               vskip_mask: Optional[torch.Tensor], Bc: int, lam: float, num_splits: int,
+                               stream: Optional[torch.cuda.Stream] = None) -> None:
+    """blasst_decode_step with the partials in the library's own per-GPU array: allocates nothing."""
+    B, Hq, one, d = q.shape
+    Hkv, N = k.shape[1], k.shape[2]
+    _need(q, "q", torch.bfloat16)
+    _need(k, "k", torch.bfloat16)
+    _need(v, "v", torch.bfloat16)
+    _need(o, "o", torch.float32)
+    if one != 1 or v.shape != k.shape or o.shape != (B, Hq, d) or (lse is not None and lse.shape != (B, Hq)):
+        raise ValueError("q [B,Hq,1,d], k and v [B,Hkv,N,d], o [B,Hq,d], lse [B,Hq]")
+    if lse is not None:
+        _need(lse, "lse", torch.float32)
+    nk = -(-N // Bc)
+    for t, shp, nm in ((skip_mask, (B, Hq, nk), "skip_mask"), (vskip_mask, (B, Hkv, nk), "vskip_mask")):
+        if t is not None:
+            _need(t, nm, torch.uint8)
+            if t.shape != shp:
+                raise ValueError("%s must be %s" % (nm, shp))
+    st = _load().blasst_decode_step_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(skip_mask),
+                                            _ptr(vskip_mask), B, Hq, N, d, Hq // Hkv, Bc, float(lam), 1, num_splits,
+                                            _stream(stream))
+    _check("blasst_decode_step_noalloc", st)
+
+
+def decode_step_noalloc_max_bytes() -> int:
+    return int(_load().blasst_decode_step_noalloc_max_bytes())
 
 
 def decode_step(q, k, v, lam: float, num_splits: int, Bc: int = 128, with_masks: bool = True):

@@ -245,6 +245,28 @@ BLASST_EXPORT blasst_status blasst_decode_step(const void* q, const void* k, con
                             causal, num_splits, stream);
 }
 
+BLASST_EXPORT size_t blasst_decode_step_noalloc_max_bytes(void) { return blasst::kDecodeScratchBytes; }
+
+BLASST_EXPORT blasst_status blasst_decode_step_noalloc(const void* q, const void* k, const void* v, float* o,
+                                                       float* lse, uint8_t* skip_mask, uint8_t* vskip_mask, int B,
+                                                       int Hq, int N, int d, int gqa_ratio, int Bc, double lambda,
+                                                       int causal, int num_splits, blasst_stream_t stream) {
+    blasst_status st = step_args_ok(o, B, Hq, d, num_splits);
+    if (st == BLASST_OK)
+        st = decode_impl(q, k, v, nullptr, nullptr, skip_mask, vskip_mask, nullptr, B, Hq, N, d, gqa_ratio, Bc, lambda,
+                         causal, num_splits, stream, false, true);
+    if (st != BLASST_OK || (int64_t)B * Hq == 0) return st;
+    if (step_workspace_bytes(B, Hq, d, num_splits) > blasst::kDecodeScratchBytes) return BLASST_ERR_UNSUPPORTED;
+    void* ws = nullptr;
+    try {
+        if (blasst::decode_scratch(&ws) != hipSuccess) return BLASST_ERR_HIP;
+    } catch (...) {
+        return BLASST_ERR_INTERNAL;
+    }
+    return decode_step_impl(q, k, v, o, lse, skip_mask, vskip_mask, ws, B, Hq, N, d, gqa_ratio, Bc, lambda, causal,
+                            num_splits, stream);
+}
+
 BLASST_EXPORT blasst_status blasst_decode_combine(const float* o_part, const float* lse_part, float* o, float* lse,
                                                   int B, int Hq, int d, int num_splits, blasst_stream_t stream) {
     try {

@@ -42,6 +42,7 @@
 #include "device_common.h"
 #include "kernels.h"
 #include <climits>
+#include <mutex>
 
 namespace blasst {
 
@@ -1008,6 +1009,36 @@ hipError_t launch_split_nt(const DecodeArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+// Scratch of the allocation-free decode step: the split partials (o_part, then
+// lse_part) of blasst_decode_step_noalloc, one copy per GPU, held until the
+// process ends.  In host code `scratch` names a host-side stand-in, not device
+// memory: the device address comes from hipGetSymbolAddress, looked up once
+// per device (with that device current) and kept in scratch_ptr.
+static __device__ __align__(256) char scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void* scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    if (scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        scratch_ptr[dev] = p;
+    }
+    *ptr = scratch_ptr[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_decode(const DecodeArgs& a, int d, int Bc, hipStream_t stream) {
     if (d == 128) return Bc == 128 ? launch_split_nt<128, 128>(a, stream) : launch_split_nt<128, 64>(a, stream);

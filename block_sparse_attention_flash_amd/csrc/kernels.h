@@ -52,6 +52,10 @@ struct MlaArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs& a, int d, int Bc, hipStream_t stream);
+// Bytes of the per-device scratch of the allocation-free decode step.
+constexpr size_t kDecodeScratchBytes = (size_t)32 << 20;
+// The current device's scratch (device address, 256-byte aligned, kDecodeScratchBytes long).
+hipError_t decode_scratch(void** ptr);
 // Dense split-KV decode, K and V streamed together (no skip test); G <= 32, plain batches.
 hipError_t launch_decode_dense(const DecodeArgs& a, int d, int Bc, hipStream_t stream);
 // Measurement only: the loads of the split kernel's two-workgroups-per-split layout at lambda = 0, nothing else.

@@ -162,6 +162,29 @@ blasst_status blasst_decode_step(const void* q, const void* k, const void* v, fl
                                  int num_splits, blasst_stream_t stream);
 
 /*
+ * blasst_decode_step_noalloc: blasst_decode_step for callers that cannot
+ * allocate device memory -- code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  It allocates nothing (no hipMalloc,
+ * no hipFree, no allocating library call): the split partials live in a
+ * static device array of the library, one per GPU, of
+ * blasst_decode_step_noalloc_max_bytes() = 32 MiB, held until the process
+ * ends.  Arguments as blasst_decode_step without the workspace; the current
+ * device's array is used, so `stream` must belong to the current device.
+ * Errors: as blasst_decode_step, plus UNSUPPORTED when the partials,
+ * B*Hq*num_splits*(d+1)*4 bytes, exceed the array; HIP if the array's device
+ * address cannot be looked up.
+ * Every call on one GPU shares that GPU's array, and the array keeps the last
+ * call's partials (every call writes all of the partials it reads, so nothing
+ * must start at zero): calls that overlap on one GPU (on different streams, or
+ * from several host threads) race and must be ordered by the caller.
+ */
+size_t blasst_decode_step_noalloc_max_bytes(void);
+blasst_status blasst_decode_step_noalloc(const void* q, const void* k, const void* v, float* o, float* lse,
+                                         uint8_t* skip_mask, uint8_t* vskip_mask, int B, int Hq, int N, int d,
+                                         int gqa_ratio, int Bc, double lambda, int causal, int num_splits,
+                                         blasst_stream_t stream);
+
+/*
  * blasst_decode_load_ceiling -- a measurement call, not part of any result.
  * Issues exactly the HBM reads blasst_decode's kernel issues at lambda = 0 in
  * its two-workgroups-per-split layout (every K row of a split read by both

@@ -29,7 +29,8 @@ def lib():
 def test_header_declares_the_entry_points():
     assert declared() == ["blasst_decode", "blasst_decode_combine", "blasst_decode_dense",
                           "blasst_decode_load_ceiling", "blasst_decode_margins", "blasst_decode_mla",
-                          "blasst_decode_ragged", "blasst_decode_step", "blasst_decode_step_workspace_size",
+                          "blasst_decode_ragged", "blasst_decode_step", "blasst_decode_step_noalloc",
+                          "blasst_decode_step_noalloc_max_bytes", "blasst_decode_step_workspace_size",
                           "blasst_prefill", "blasst_prefill_dense", "blasst_prefill_margins", "blasst_prefill_ragged",
                           "blasst_status_string"]
 
@@ -222,3 +223,17 @@ def test_decode_step_validates_its_workspace(lib):
     assert call(S=3, ws_bytes=10**6) == 1         # 3 splits > 2 blocks
     assert call(lam=1.0) == 1
     assert call(B=0, ws=None, o=None) == 0        # empty batch: validated, nothing launched
+
+
+def test_decode_step_noalloc_validates_before_touching_hip(lib):
+    cap = lib.blasst_decode_step_noalloc_max_bytes
+    cap.argtypes = []
+    cap.restype = ctypes.c_size_t
+    assert cap() == 32 << 20
+    f = lib.blasst_decode_step_noalloc
+    f.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, D, I, I, P]
+    assert f(FAKE, FAKE, FAKE, None, None, None, None, 1, 4, 256, 128, 4, 128, 1e-3, 1, 2, None) == 1  # NULL o
+    assert f(FAKE, FAKE, FAKE, FAKE, None, None, None, 1, 4, 256, 128, 4, 128, 2.0, 1, 2, None) == 1   # lambda
+    # partials of 64 x 64 heads x 16 splits x 129 fp32 exceed the 32 MiB array: rejected before any HIP call
+    assert f(FAKE, FAKE, FAKE, FAKE, None, None, None, 64, 64, 2048, 128, 64, 128, 1e-3, 1, 16, None) == 2
+    assert f(FAKE, FAKE, FAKE, FAKE, None, None, None, 0, 4, 256, 128, 4, 128, 1e-3, 1, 2, None) == 0  # empty batch
