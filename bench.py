@@ -40,8 +40,8 @@ METRIC = "decode µs & HBM GB/s at 32K; prefill TFLOP/s at 32K; block sparsity %
 # (profiles/*.md, a "key: value" block).  A record counts only while the
 # kernel's sources hash to the value it was taken with.
 KERNEL_SOURCES = {
-    "decode_split_kernel": ["decode.hip", "device_common.h", "kernels.h"],
-    "prefill_kernel": ["prefill.hip", "device_common.h", "kernels.h"],
+    "decode_split_kernel": ["decode.hip", "device_common.h", "tile_copy.h", "kernels.h"],
+    "prefill_kernel": ["prefill.hip", "device_common.h", "tile_copy.h", "kernels.h"],
 }
 
 

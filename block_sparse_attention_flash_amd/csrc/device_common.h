@@ -15,6 +15,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "tile_copy.h"  // chunk_swizzle and the tile-copy offsets (host-callable)
+
 namespace blasst {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -73,22 +75,6 @@ __device__ __forceinline__ bf16x8 lds_read_tr16_pair(const lds_char* lo, const l
     typedef short i16x8 __attribute__((ext_vector_type(8)));
     const i16x8 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
     return __builtin_bit_cast(bf16x8, ab);
-}
-
-// XOR mask applied to the 16-byte chunk index of row r of a K/V tile in LDS.
-// With 16 chunks per row (256-byte rows) it is the GF(2)-linear map sending the
-// row's bits 0..3 to 4, 10, 1, 2; with 8 chunks per row, bits 0..2 to 2, 4, 1.
-// An exhaustive search over such maps found these conflict-free (256-byte
-// rows) or least-conflicting (128-byte rows) for both access patterns used on
-// the tiles -- 32 consecutive rows x one chunk (ds_read_b128, MFMA A rows) and
-// 4 consecutive rows x two chunks per 16 lanes (ds_read_b64_tr_b16) -- whether
-// the LDS serves 32 or 64 banks per cycle.
-template <int CPR>
-__device__ __forceinline__ constexpr int chunk_swizzle(int r) {
-    if constexpr (CPR == 16)
-        return ((r & 1) * 4) ^ (((r >> 1) & 1) * 10) ^ ((r >> 2) & 1) ^ (((r >> 3) & 1) * 2);
-    else
-        return ((r & 1) * 2) ^ (((r >> 1) & 1) * 4) ^ ((r >> 2) & 1);
 }
 
 // LDS byte address of a pointer into a __shared__ array.

@@ -189,17 +189,13 @@ __global__ __launch_bounds__(2 * BC * HPW) void prefill_kernel(PrefillArgs a) {
     //      wave-uniform.  Only a ragged last tile clamps its rows to T - 1.
     uint32_t toff[CPW];
 #pragma unroll
-    for (int f = 0; f < CPW; ++f) {
-        const int pp = (wave * CPW + f) * 64 + lane;
-        toff[f] = (uint32_t)((pp / CPR) * ROWB + (((pp % CPR) ^ chunk_swizzle<CPR>(pp / CPR)) << 4));
-    }
+    for (int f = 0; f < CPW; ++f) toff[f] = tile_copy_offset<CPR>(wave, CPW, f, lane);
     auto issue = [&](const uint16_t* base, char* lds_tile, int j) {
         const uint16_t* tbase = base + (size_t)j * BC * D;
-        const bool ragged = (j + 1) * BC > T;
+        const bool ragged = tile_is_ragged<BC>(j, T);
 #pragma unroll
         for (int f = 0; f < CPW; ++f) {
-            uint32_t off = toff[f];
-            if (ragged) off -= (uint32_t)(max(j * BC + (int)(off / ROWB) - (T - 1), 0) * ROWB);
+            const uint32_t off = ragged ? tile_copy_clamp<CPR, BC>(toff[f], j, T) : toff[f];
             global_to_lds16_sbase(tbase, off, lds_addr(lds_tile + (wave * CPW + f) * 1024));
         }
     };
@@ -512,17 +508,13 @@ __global__ __launch_bounds__(2 * BC) void prefill_margin_kernel(PrefillArgs a) {
 
     uint32_t toff[CPW];
 #pragma unroll
-    for (int f = 0; f < CPW; ++f) {
-        const int pp = (wave * CPW + f) * 64 + lane;
-        toff[f] = (uint32_t)((pp / CPR) * ROWB + (((pp % CPR) ^ chunk_swizzle<CPR>(pp / CPR)) << 4));
-    }
+    for (int f = 0; f < CPW; ++f) toff[f] = tile_copy_offset<CPR>(wave, CPW, f, lane);
     auto issue_k = [&](int j) {
         const uint16_t* tbase = kbase + (size_t)j * BC * D;
-        const bool ragged = (j + 1) * BC > T;
+        const bool ragged = tile_is_ragged<BC>(j, T);
 #pragma unroll
         for (int f = 0; f < CPW; ++f) {
-            uint32_t off = toff[f];
-            if (ragged) off -= (uint32_t)(max(j * BC + (int)(off / ROWB) - (T - 1), 0) * ROWB);
+            const uint32_t off = ragged ? tile_copy_clamp<CPR, BC>(toff[f], j, T) : toff[f];
             global_to_lds16_sbase(tbase, off, lds_addr(&lds_k[j & 1][(wave * CPW + f) * 1024]));
         }
     };
