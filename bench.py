@@ -94,7 +94,8 @@ def parse():
                                                  "decode_sweep128", "prefill", "copy"], default=None,
                    help="run only one kernel a few times (for hardware-counter collection) and exit")
     p.add_argument("--profile-lambda", type=float, default=None,
-                   help="lambda for --profile-target decode_sweep128 (default: the split kernel's lambda = 0)")
+                   help="lambda for --profile-target decode / decode_mqa (default: the workload's) and "
+                        "decode_sweep128 (default 0)")
     p.add_argument("--profile-launches", type=int, default=10)
     p.add_argument("--length-sweep", action="store_true",
                    help="instead of the bench: sparsity drift over 4K-128K context and the lambda = a/L calibration")
@@ -142,6 +143,8 @@ def profile_target(args, lib, torch, W):
             w = w.with_(lambdas=(args.profile_lambda or 0.0,))
         else:
             w = W.CONFIGS["decode_32k" if args.profile_target == "decode" else "decode_mqa_16k"]
+            if args.profile_lambda is not None:
+                w = w.with_(lambdas=(args.profile_lambda,))
         ncopies = 1 if args.profile_target == "decode_sweep128" else max(1, args.copies)
         copies = [{k: dev(v) for k, v in W.generate(w).items()} for _ in range(ncopies)]
         B, Hq, N, d, Bc, S = w.B, w.Hq, w.T, w.d, w.Bc, w.num_splits
@@ -186,10 +189,12 @@ SWEEP_FIXED = (1e-3, 3e-3)
 SWEEP_TARGETS = (0.5, 0.7)
 
 
-def sweep_margins(kind, L, split, W, bsa, B=None):
+def sweep_margins(kind, L, split, W, bsa, B=None, num_splits=None):
     """GPU decision margins of one length-sweep batch (flattened) and the margin kernel's time."""
     import torch
     w = W.sweep_workload(kind, L, split, B)
+    if num_splits is not None:
+        w = w.with_(num_splits=num_splits)
     x = W.generate(w, parts=("q", "k"))
     q, k = dev(x["q"]), dev(x["k"])
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -627,12 +632,14 @@ def bench_ragged(args, lib, torch, W):
     return {"decode_serving_batch": dec, "prefill_causal": pre}
 
 
-def calibrate_decode_policy(W, bsa, B=None):
+def calibrate_decode_policy(W, bsa, B=None, num_splits=1):
     """lambda = a/L for decode, fitted on the calibration sequences of the length-sweep family
-    (4K-64K, one split, GPU margins): returns (alpha, beta, number of points)."""
+    (4K-64K, GPU margins at num_splits splits): returns (alpha, beta, number of points).  A split
+    restarts the running max, so the margins -- and the lambda a target sparsity needs -- depend
+    on the split count; the fit is taken at the count the kernel then runs with."""
     from block_sparse_attention_flash_amd import policy
     lengths = W.SWEEP_LENGTHS[:5]
-    margins = [sweep_margins("decode", L, "calibration", W, bsa, B)[0] for L in lengths]
+    margins = [sweep_margins("decode", L, "calibration", W, bsa, B, num_splits)[0] for L in lengths]
     a, s = policy.calibration_points(margins, list(lengths), SWEEP_LAMBDAS)
     alpha, beta = policy.fit_exponential(a, s)
     return alpha, beta, int(len(a))
@@ -641,13 +648,12 @@ def calibrate_decode_policy(W, bsa, B=None):
 def bench_decode_length_sweep(args, lib, torch, W, bsa):
     """What a decode skip buys where skipping is common: the length-sweep family's held-out 128K
     sequences (B = 4, Hq = 32, Hkv = 8, d = 128), split 4 ways (128 units: the two-workgroups-per-split
-    layout fills the GPU, and each split's running max sees 256 blocks, close to the one-split margins
-    the policy is fitted on; a split restarts the max, so 16 splits skip far less), timed through the split kernel at
-    lambda = a/L for 50% and 70% target sparsity (a fitted on the 4K-64K calibration sequences) and at
+    layout fills the GPU), timed through the split kernel at lambda = a/L for 50% and 70% target
+    sparsity (a fitted on the 4K-64K calibration sequences' margins at the same split count) and at
     fixed lambdas, against lambda = 0 and the dense kernel.  The split kernel reads all of K and the kept
     V blocks, so the bytes predict the speed-up: 1 / (1 - vload * V / (K + V))."""
     from block_sparse_attention_flash_amd import policy
-    alpha, beta, npts = calibrate_decode_policy(W, bsa)
+    alpha, beta, npts = calibrate_decode_policy(W, bsa, num_splits=SWEEP128_SPLITS)
     L = W.SWEEP_LENGTHS[-1]
     w = W.sweep_workload("decode", L, "evaluation").with_(num_splits=SWEEP128_SPLITS)
     x = {k: dev(v) for k, v in W.generate(w).items()}
@@ -707,7 +713,8 @@ def bench_decode_length_sweep(args, lib, torch, W, bsa):
     del x
     torch.cuda.empty_cache()
     return dict(workload=w.name, B=B, Hq=Hq, Hkv=w.Hkv, d=d, context=N, Bc=Bc, num_splits=S,
-                policy={"alpha": alpha, "beta": beta, "points": npts, "calibration_lengths": list(W.SWEEP_LENGTHS[:5])},
+                policy={"alpha": alpha, "beta": beta, "points": npts, "calibration_lengths": list(W.SWEEP_LENGTHS[:5]),
+                        "calibration_splits": SWEEP128_SPLITS},
                 dense_kernel_us=round(dense_ms[0] * 1e3, 2), by_lambda=rows)
 
 
