@@ -86,21 +86,31 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // lds_base + 16*l, lds_base being wave-uniform (it travels in M0).  Issued as
 // inline asm so the compiler adds no wait of its own for the LDS bytes it cannot
 // see; the caller waits with an explicit, counted s_waitcnt vmcnt.
+// The compiler's hazard pass cannot see that the asm is an LDS-DMA load, so the
+// wait states this family needs before it are in the asm itself: one after a
+// scalar write of M0 (which the compiler emits right before the asm).
 __device__ __forceinline__ void global_to_lds16(const void* gptr, uint32_t lds_base) {
-    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(__builtin_amdgcn_readfirstlane(lds_base))
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr),
+                 "{m0}"(__builtin_amdgcn_readfirstlane(lds_base))
                  : "memory");
 }
 
 // Same copy with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane byte
 // offset (the instruction's saddr form): one VGPR of address per lane.
 // The base must be the same in every lane; readfirstlane states that to the
-// compiler (it cannot always prove it) so the operand is an SGPR pair.
+// compiler (it cannot always prove it) so the operand is an SGPR pair.  A VMEM
+// instruction that reads an SGPR written by a VALU instruction (v_readfirstlane)
+// needs five wait states in between, which the compiler cannot insert for an
+// asm it does not look into; without them the copy can read a stale base (a
+// wild address) wherever the compiler places the readfirstlane right before
+// it, so the asm starts with them (they also cover the scalar write of M0).
 __device__ __forceinline__ void global_to_lds16_sbase(const void* sbase, uint32_t voff, uint32_t lds_base) {
     const uint64_t p = (uint64_t)sbase;
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)p);
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
     const void* sp = (const void*)(((uint64_t)hi << 32) | lo);
-    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sp), "{m0}"(__builtin_amdgcn_readfirstlane(lds_base))
+    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sp),
+                 "{m0}"(__builtin_amdgcn_readfirstlane(lds_base))
                  : "memory");
 }
 

@@ -45,6 +45,7 @@ constexpr int PRIO_Y = BLASST_PREFILL_PRIO_Y;
 #define BLASST_PREFILL_PFV 2
 #endif
 constexpr int PFV = BLASST_PREFILL_PFV;  // V^T prefetch distance in 16-key sub-tiles
+constexpr float kLagLog2 = 8.f;          // how far (log2 units) the softmax reference may trail the max
 
 // SKIP = false builds the same kernel without the skip test (every tile kept,
 // no vote): the dense reference the test's cost is measured against.
@@ -181,7 +182,12 @@ __global__ __launch_bounds__(2 * BC * HPW) void prefill_kernel(PrefillArgs a) {
     f32x16 oacc[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
-    float m = kNegInf, l = 0.f;  // m in raw (unscaled) score units
+    // m: the row's running max (raw, unscaled score units), which the skip test reads;
+    // mref: the max the exponentials and (O, l) are currently taken against.  mref trails m by
+    // at most kLagLog2 in log2 units, so O and l are rescaled only when some row's max has
+    // moved that far (P = 2^(s c - mref c) then stays below 2^kLagLog2, exact in range for
+    // bf16 and fp32); the result O / l and the LSE mref c ln 2 + ln l do not depend on mref.
+    float m = kNegInf, mref = kNegInf, l = 0.f;
 
     // ---- tile copies: this wave's 1 KiB pieces, LDS position pp -> row pp / CPR,
     //      physical chunk pp % CPR holding logical chunk (pp % CPR) ^ swizzle(row).
@@ -192,11 +198,16 @@ __global__ __launch_bounds__(2 * BC * HPW) void prefill_kernel(PrefillArgs a) {
     for (int f = 0; f < CPW; ++f) toff[f] = tile_copy_offset<CPR>(wave, CPW, f, lane);
     auto issue = [&](const uint16_t* base, char* lds_tile, int j) {
         const uint16_t* tbase = base + (size_t)j * BC * D;
-        const bool ragged = tile_is_ragged<BC>(j, T);
+        if (__builtin_expect(tile_is_ragged<BC>(j, T), 0)) {
+            // only a last tile running past the sequence clamps its rows (a wave-uniform branch)
 #pragma unroll
-        for (int f = 0; f < CPW; ++f) {
-            const uint32_t off = ragged ? tile_copy_clamp<CPR, BC>(toff[f], j, T) : toff[f];
-            global_to_lds16_sbase(tbase, off, lds_addr(lds_tile + (wave * CPW + f) * 1024));
+            for (int f = 0; f < CPW; ++f)
+                global_to_lds16_sbase(tbase, tile_copy_clamp<CPR, BC>(toff[f], j, T),
+                                      lds_addr(lds_tile + (wave * CPW + f) * 1024));
+        } else {
+#pragma unroll
+            for (int f = 0; f < CPW; ++f)
+                global_to_lds16_sbase(tbase, toff[f], lds_addr(lds_tile + (wave * CPW + f) * 1024));
         }
     };
     auto issue_k = [&](int j, int stage) { issue(kbase, &lds_k[stage][0], j); };
@@ -295,14 +306,17 @@ __global__ __launch_bounds__(2 * BC * HPW) void prefill_kernel(PrefillArgs a) {
         }
         if (wrow == 0 && lane == 0 && mask_row) mask_row[j] = (uint8_t)skip;
         if (skip) return;
-        if (!__all(m_new == m)) {  // rescale only when some row's max moved
-            const float alpha = exp2_fast((m - m_new) * c);
+        if (!__all(m_new == mref || (m_new - mref) * c <= kLagLog2)) {
+            // some row's max moved more than kLagLog2 past its reference: every row moves its
+            // reference to its running max (a row still at -inf keeps factor 1)
+            const float alpha = m_new == mref ? 1.f : exp2_fast((mref - m_new) * c);
             l *= alpha;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+            mref = m_new;
         }
         m = m_new;
-        const float mc = m * c;
+        const float mc = mref * c;
         const char* vt_base = &lds_v[j & 1][0];
         // Software-pipelined over the 2*KT sub-tiles of 16 keys: P of sub-tile
         // u + 1 (exp, row sum, bf16 pack) is formed between the four PV MFMAs of
@@ -419,7 +433,7 @@ __global__ __launch_bounds__(2 * BC * HPW) void prefill_kernel(PrefillArgs a) {
                 *(f32x4*)(orow + 32 * dt + 8 * eg + 4 * half) =
                     f32x4{oacc[dt][4 * eg] * inv, oacc[dt][4 * eg + 1] * inv, oacc[dt][4 * eg + 2] * inv,
                           oacc[dt][4 * eg + 3] * inv};
-        if (half == 0 && a.lse) a.lse[((size_t)b * a.Hq + hq) * Tcap + qidx] = row_ok ? m * c * kLn2 + logf(l) : kNegInf;
+        if (half == 0 && a.lse) a.lse[((size_t)b * a.Hq + hq) * Tcap + qidx] = row_ok ? mref * c * kLn2 + logf(l) : kNegInf;
     }
     if (mask_row && wrow == 0)
         for (int j = jend + lane; j < a.nk; j += 64) mask_row[j] = 2;
