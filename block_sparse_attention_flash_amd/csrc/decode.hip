@@ -48,6 +48,8 @@ namespace blasst {
 
 namespace {
 
+constexpr float LAZY_LAG = 8.f;  // how far (log2 units) a head's softmax reference may trail its max
+
 // s_waitcnt vmcnt(F * n) for a wave-uniform n in 0..3 (the count is an immediate)
 template <int F>
 __device__ __forceinline__ void wait_vm(int n) {
@@ -181,10 +183,17 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
     bool q_staged = !QL;
 
     f32x4 oacc[NT][DTV];
-    float m_run[NT], l_part[NT];
+    // m_run: the head's running max (log2 units), which the decisions continue;
+    // mref: the max P and (O, l) are currently taken against.  mref trails m_run by
+    // at most LAZY_LAG, so the phase's rescale of O and l (VALU work on the
+    // accumulators, which live partly in AGPRs) runs only when some head's max has
+    // moved that far; P = 2^(t - mref) then stays below 2^LAZY_LAG, exact in range
+    // for bf16 and fp32, and O / l and the LSE mref ln 2 + ln l do not depend on mref.
+    float m_run[NT], mref[NT], l_part[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         m_run[nt] = kNegInf;
+        mref[nt] = kNegInf;
         l_part[nt] = 0.f;
 #pragma unroll
         for (int dt = 0; dt < DTV; ++dt) oacc[nt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -387,12 +396,12 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
         // ================= decide (the blocks not decided early) =================
         decide(BE, BPP);
         uint32_t vkeep = 0;
-        float alpha[NT];
+        bool lag = false;  // some head's max ran more than LAZY_LAG past its reference
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             vkeep |= keep[nt];
-            alpha[nt] = head_ok[nt] ? exp2_fast(m_run[nt] - m_dec[nt]) : 1.f;
             m_run[nt] = head_ok[nt] ? m_dec[nt] : m_run[nt];
+            lag |= !(m_run[nt] == mref[nt] || m_run[nt] - mref[nt] <= LAZY_LAG);
         }
         vkeep = row16_or(vkeep);
         if constexpr (MARGINS) {
@@ -442,12 +451,19 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
                 if ((km >> u) & 1u) issue_v(u);
         }
 
-        // rescale the running state to the phase's new max (overlaps the V loads)
+        // move every head's reference to its running max when one has run too far
+        // ahead (overlaps the V loads).  Each wave holds every head in the same
+        // lanes and the same m_run, mref, so all waves take the branch together and
+        // keep one reference per head: their partial O and l are summed at the end.
+        if (__any(lag)) {
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            l_part[nt] *= alpha[nt];
+            for (int nt = 0; nt < NT; ++nt) {
+                const float alpha = m_run[nt] == mref[nt] ? 1.f : exp2_fast(mref[nt] - m_run[nt]);
+                l_part[nt] *= alpha;
 #pragma unroll
-            for (int dt = 0; dt < DTV; ++dt) oacc[nt][dt] *= alpha[nt];
+                for (int dt = 0; dt < DTV; ++dt) oacc[nt][dt] *= alpha;
+                mref[nt] = m_run[nt];
+            }
         }
 
 #pragma unroll
@@ -467,7 +483,7 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
                     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            const float e = exp2_fast(t[u][kt][nt][i] - m_run[nt]);
+                            const float e = exp2_fast(t[u][kt][nt][i] - mref[nt]);
                             p[4 * kt + i] = kp ? e : 0.f;
                         }
                     l_part[nt] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
@@ -525,7 +541,7 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
                 }
                 *(f32x4*)(a.o_part + orow * D + half * DV + 16 * dt + 4 * g) = f32x4{o4[0], o4[1], o4[2], o4[3]};
             }
-            if (wave == 0 && g == 0 && half == 0) a.lse_part[orow] = m_run[nt] * kLn2 + logf(lt);
+            if (wave == 0 && g == 0 && half == 0) a.lse_part[orow] = mref[nt] * kLn2 + logf(lt);
         }
         __syncthreads();
     }
