@@ -547,6 +547,297 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
     }
 }
 
+// Wide-group decode: one kv head shared by 33..64 query heads (MQA and wide
+// GQA), d = 128.  The decisions and the skip rule are those of
+// decode_split_kernel (Eq. 5 of the BLASST blog on the prefix max of the block
+// maxima, no cascade; V copied only for blocks some head keeps); the work is
+// laid out differently, because 64 heads' worth of O^T per wave (128 fp32 per
+// lane) leaves one wave per SIMD and forces the accumulators through the AGPR
+// file.  A block of BC keys is split over the eight waves two ways:
+//   S^T = K q^T    wave w forms the scores of 32-key unit us and 16-head tiles
+//                  st0 .. st0 + SNT - 1 of the block (q^T in registers), and
+//                  publishes each (unit, head) maximum in LDS;
+//   decisions      every wave reads the block maxima of all 64 heads and runs
+//                  the same prefix max, so the V copy (issued only when some
+//                  head keeps the block) and the rescale branch are uniform;
+//   P              the wave's exponentials go to LDS in the MFMA B-operand
+//                  layout (bf16, 16-byte chunks XOR-swizzled by head);
+//   O^T += V^T P^T wave w owns d rows 16 w .. 16 w + 15 of O^T for every head,
+//                  over all of the block's units (V^T read back transposed).
+// So each lane holds 16 O^T values, and two waves share each SIMD.
+// Software pipeline: step jj forms S, the decisions and P of block jj and
+// issues V(jj), then forms O for block jj - 1, whose V copy has had a whole
+// step to land (a V copy can only start once its block is decided).  K runs
+// two blocks ahead through a two-slot ring, V through two slots, and P of
+// block jj waits in registers until step jj + 1, when every wave is done with
+// P of block jj - 1.  A rescale from block jj's decisions is applied to O only
+// after O has taken block jj - 1 (whose P used the previous reference).
+template <int BC>
+__global__ __launch_bounds__(512) void decode_wide_kernel(DecodeArgs a) {
+    constexpr int D = 128;
+    constexpr int W = 8;                   // waves; wave w forms O^T rows 16 w .. 16 w + 15
+    constexpr int KG = BC / 32;            // 32-key units per block
+    constexpr int NT = 4;                  // 16-head tiles (64 heads)
+    constexpr int SNT = NT * KG / W;       // S head tiles per wave
+    constexpr int DS = D / 32;             // MFMA k-steps over d for S
+    constexpr int CPR = D / 8;             // 16-byte chunks per K/V row
+    constexpr int ROWB = 2 * D;            // bytes per K/V row
+    constexpr int TILE = BC * ROWB;        // bytes of a K or V block
+    constexpr int CPW = TILE / (1024 * W); // 1 KiB copies per wave per block
+    static_assert(SNT >= 1 && (NT * KG) % W == 0 && TILE % (1024 * W) == 0, "work must split evenly");
+    static_assert(W * 16 == D, "one 16-row O^T tile per wave");
+
+    __shared__ __attribute__((aligned(16))) char lds_k[2][TILE];
+    __shared__ __attribute__((aligned(16))) char lds_v[2][TILE];
+    __shared__ __attribute__((aligned(16))) char lds_p[KG * 64 * 64];  // [unit][head][32 keys] bf16
+    __shared__ float lds_pmax[KG][64];
+    float(*lds_l)[64] = (float(*)[64])lds_p;  // [W][64] after the last step
+
+    const int split = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int g = lane >> 4, n = lane & 15;
+    const int G = a.G, N = a.N, nk = a.nk;
+    const int j0 = (int)((int64_t)split * nk / a.S);
+    const int j1 = (int)((int64_t)(split + 1) * nk / a.S);
+    const uint16_t* kbase = a.k + ((size_t)b * a.Hkv + hkv) * (size_t)N * D;
+    const uint16_t* vbase = a.v + ((size_t)b * a.Hkv + hkv) * (size_t)N * D;
+
+    // this wave's S items: unit us of the block, head tiles st0 .. st0 + SNT - 1
+    const int us = wave / (NT / SNT);
+    const int st0 = (wave % (NT / SNT)) * SNT;
+    bool head_ok[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) head_ok[nt] = nt * 16 + n < G;
+
+    // q^T as the S B operand: lane (g, n) holds q[head][32 s + 8 g .. + 8] (zero past G)
+    bf16x8 qf[SNT][DS];
+#pragma unroll
+    for (int i = 0; i < SNT; ++i) {
+        const int h = (st0 + i) * 16 + n;
+        const uint16_t* qrow = a.q + ((size_t)b * a.Hq + (size_t)hkv * G + (h < G ? h : 0)) * D;
+#pragma unroll
+        for (int s = 0; s < DS; ++s)
+            qf[i][s] = as_bf16x8(h < G ? load16(qrow + 32 * s + 8 * g) : u32x4{0u, 0u, 0u, 0u});
+    }
+
+    // m_run: each head's running max (log2 units); mref: the max P and (O, l) are
+    // taken against, trailing m_run by at most LAZY_LAG (as in decode_split_kernel);
+    // l_own: the row sums of this wave's S items
+    f32x4 oacc[NT];
+    float m_run[NT], mref[NT], l_own[SNT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        oacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m_run[nt] = kNegInf;
+        mref[nt] = kNegInf;
+    }
+#pragma unroll
+    for (int i = 0; i < SNT; ++i) l_own[i] = 0.f;
+
+    // block j of K or V -> a tile: copy f of this wave moves 16 bytes per lane (a
+    // fixed byte offset inside the block, chunk x of tile row r landing at
+    // x ^ (r mod CPR)) from a wave-uniform block base in SGPRs; only a last block
+    // running past the context re-reads key N - 1 in place of the missing rows
+    // (their scores are masked)
+    uint32_t toff[CPW];
+#pragma unroll
+    for (int f = 0; f < CPW; ++f) toff[f] = tile_copy_offset_rowxor<CPR>(wave, CPW, f, lane);
+    auto issue = [&](const uint16_t* base, char* tile, int j) {
+        const uint16_t* tbase = base + (size_t)j * BC * D;
+        if (__builtin_expect(tile_is_ragged<BC>(j, N), 0)) {
+#pragma unroll
+            for (int f = 0; f < CPW; ++f)
+                global_to_lds16_sbase(tbase, tile_copy_clamp<CPR, BC>(toff[f], j, N),
+                                      lds_addr(tile + (wave * CPW + f) * 1024));
+        } else {
+#pragma unroll
+            for (int f = 0; f < CPW; ++f)
+                global_to_lds16_sbase(tbase, toff[f], lds_addr(tile + (wave * CPW + f) * 1024));
+        }
+    };
+    if (j0 < j1) issue(kbase, lds_k[0], j0);
+    if (j0 + 1 < j1) issue(kbase, lds_k[1], j0 + 1);
+    wait_vm<CPW>(j0 + 1 < j1 ? 1 : 0);  // this wave's K(j0) copies
+    __syncthreads();
+
+    u32x4 pr[SNT];             // P of the block formed last step, for the LDS
+    bool vkeep_prev = false;   // the block formed last step is kept by some head
+    for (int jj = j0; jj <= j1; ++jj) {
+        const bool front = jj < j1;  // block jj: S, decisions, P, V copy
+        const int x = (jj - j0) & 1;  // ring slot of block jj
+        float t[SNT][2][4];           // raw scores of keys 16 kt + 4 g + e of unit us, head (st0 + i) * 16 + n
+        if (front) {
+            // ---- S^T = K q^T: A = K rows 16 kt + n of unit us (chunk 4 s + g), B = q^T
+            const char* kt_base = lds_k[x] + us * 32 * ROWB;
+            u32x4 kf[2][DS];
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int s = 0; s < DS; ++s) {
+                    const int r = 16 * kt + n, c = 4 * s + g;
+                    kf[kt][s] = *(const u32x4*)(kt_base + r * ROWB + ((c ^ (r & (CPR - 1))) << 4));
+                }
+            const bool tail = tile_is_ragged<BC>(jj, N);  // keys past the context are masked
+#pragma unroll
+            for (int i = 0; i < SNT; ++i) {
+                float pm = kNegInf;
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < DS; ++s) acc = mfma16x16x32(as_bf16x8(kf[kt][s]), qf[i][s], acc);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        float v = acc[e];
+                        if (tail) v = jj * BC + 32 * us + 16 * kt + 4 * g + e < N ? v : kNegInf;
+                        t[i][kt][e] = v;
+                        pm = fmaxf(pm, v);
+                    }
+                }
+                // over the four lane groups g; published in log2 units (the scale is positive)
+                pm = wave_max_xor32(wave_max_xor16(pm)) * a.score_scale;
+                if (g == 0) lds_pmax[us][(st0 + i) * 16 + n] = pm;
+            }
+        }
+        // block maxima published; every wave is done with K(jj)'s slot, with V(jj - 2)'s
+        // slot and with P of block jj - 2
+        __syncthreads();
+
+        if (vkeep_prev) {  // P of block jj - 1 (lane (g, n): chunk g of head n's row)
+#pragma unroll
+            for (int i = 0; i < SNT; ++i) {
+                const int h = (st0 + i) * 16 + n;
+                *(u32x4*)(lds_p + (us * 64 + h) * 64 + ((g ^ ((h >> 2) & 3)) << 4)) = pr[i];
+            }
+        }
+        bool vkeep = false, lag = false;
+        float alpha[NT];
+        int nissued = 0;  // copy groups issued this step (waited for next step)
+        if (front) {
+            // ---- decisions for all 64 heads (every wave the same): Eq. 5 on the block max
+            uint32_t keepm = 0;  // bit nt: head nt * 16 + n keeps block jj
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                float bm = kNegInf;
+#pragma unroll
+                for (int u = 0; u < KG; ++u) bm = fmaxf(bm, lds_pmax[u][nt * 16 + n]);
+                const float mn = fmaxf(m_run[nt], bm);
+                keepm |= (uint32_t)(head_ok[nt] && !((bm - mn) < a.thr)) << nt;
+                m_run[nt] = head_ok[nt] ? mn : m_run[nt];
+                lag |= !(m_run[nt] == mref[nt] || m_run[nt] - mref[nt] <= LAZY_LAG);
+            }
+            vkeep = __any(keepm != 0u);
+            lag = __any(lag);  // the same in every wave: the same lanes hold the same maxima
+            if (a.skip != nullptr && wave == 0 && g == 0) {
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+                    if (head_ok[nt])
+                        a.skip[((size_t)b * a.Hq + (size_t)hkv * G + nt * 16 + n) * nk + jj] =
+                            (uint8_t)(((keepm >> nt) & 1u) ^ 1u);
+            }
+            if (a.vskip != nullptr && threadIdx.x == 0) a.vskip[((size_t)b * a.Hkv + hkv) * nk + jj] = (uint8_t)!vkeep;
+            // K(jj + 2) into the slot K(jj) used, then V(jj) (kept blocks only)
+            if (jj + 2 < j1) {
+                issue(kbase, lds_k[x], jj + 2);
+                ++nissued;
+            }
+            if (vkeep) {
+                issue(vbase, lds_v[x], jj);
+                ++nissued;
+            }
+            // ---- lazy rescale: l now, O after it has taken block jj - 1
+            if (lag) {
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    alpha[nt] = m_run[nt] == mref[nt] ? 1.f : exp2_fast(mref[nt] - m_run[nt]);
+                    mref[nt] = m_run[nt];
+                }
+#pragma unroll
+                for (int i = 0; i < SNT; ++i) {
+                    float al = alpha[0];
+#pragma unroll
+                    for (int nt = 1; nt < NT; ++nt) al = st0 + i == nt ? alpha[nt] : al;
+                    l_own[i] *= al;
+                }
+            }
+            // ---- P of this wave's S items (held in registers until next step)
+            if (vkeep) {
+#pragma unroll
+                for (int i = 0; i < SNT; ++i) {
+                    const int nts = st0 + i;
+                    float mr = mref[0];
+#pragma unroll
+                    for (int nt = 1; nt < NT; ++nt) mr = nts == nt ? mref[nt] : mr;
+                    const bool kp = (keepm >> nts) & 1u;
+                    const float sc = a.score_scale;
+                    float p[8];
+#pragma unroll
+                    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            p[4 * kt + e] = kp ? exp2_fast(__builtin_fmaf(t[i][kt][e], sc, -mr)) : 0.f;
+                    l_own[i] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+                    pr[i] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                                  pack_bf16x2(p[6], p[7])};
+                }
+            }
+        }
+        // V(jj - 1) and K(jj + 1) (issued last step) have landed; only this step's copies may be in flight
+        wait_vm<CPW>(nissued);
+        __syncthreads();  // P and V of block jj - 1 and K(jj + 1) visible to every wave
+
+        // ---- O^T rows 16 wave .. + 15 += V^T P^T over block jj - 1's units
+        if (vkeep_prev) {
+            const char* vt = lds_v[x ^ 1];
+#pragma unroll
+            for (int u = 0; u < KG; ++u) {
+                const char* vs = vt + u * 32 * ROWB;
+                const int cc = 2 * wave + ((n & 3) >> 1);
+                const int r0 = 4 * g + (n >> 2), r1 = 16 + 4 * g + (n >> 2);
+                const u32x2 lo = lds_read_tr16((const lds_char*)(vs + r0 * ROWB + ((cc ^ (r0 & (CPR - 1))) << 4) + (n & 1) * 8));
+                const u32x2 hi = lds_read_tr16((const lds_char*)(vs + r1 * ROWB + ((cc ^ (r1 & (CPR - 1))) << 4) + (n & 1) * 8));
+                const bf16x8 av = as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y});
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    const int h = nt * 16 + n;
+                    const u32x4 pf = *(const u32x4*)(lds_p + (u * 64 + h) * 64 + ((g ^ ((h >> 2) & 3)) << 4));
+                    oacc[nt] = mfma16x16x32(av, as_bf16x8(pf), oacc[nt]);
+                }
+            }
+        }
+        if (lag) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) oacc[nt] *= alpha[nt];
+        }
+        vkeep_prev = vkeep;
+    }
+
+    // ---- l per head: the waves' sums over their S items' keys; O / l and the LSE
+    __syncthreads();  // every wave is done with P of the last block (lds_l shares its bytes)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        float ls = 0.f;  // head tiles outside this wave's S items hold 0
+#pragma unroll
+        for (int i = 0; i < SNT; ++i) ls = st0 + i == nt ? l_own[i] : ls;
+        ls = wave_sum_xor32(wave_sum_xor16(ls));
+        if (g == 0) lds_l[wave][nt * 16 + n] = ls;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        float lt = 0.f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) lt += lds_l[w][nt * 16 + n];
+        const int h = nt * 16 + n;
+        if (h < G) {
+            const size_t orow = ((size_t)b * a.Hq + (size_t)hkv * G + h) * a.S + split;
+            const float inv = lt > 0.f ? 1.f / lt : 0.f;  // 0: a split with no block
+            *(f32x4*)(a.o_part + orow * D + 16 * wave + 4 * g) = oacc[nt] * inv;
+            if (wave == 0 && g == 0) a.lse_part[orow] = mref[nt] * kLn2 + logf(lt);
+        }
+    }
+}
+
 // s_waitcnt vmcnt(F * n) for a wave-uniform n in 0..7
 template <int F>
 __device__ __forceinline__ void wait_vm8(int n) {
@@ -1003,6 +1294,13 @@ hipError_t launch_margins_nt(const DecodeArgs& a, hipStream_t stream) {
     return launch_split_heads<D, BC, 4, 2, 4, 2, 2, true>(a, stream);
 }
 
+template <int BC>
+hipError_t launch_wide(const DecodeArgs& a, hipStream_t stream) {
+    dim3 grid(a.S, a.Hkv, a.B);
+    hipLaunchKernelGGL((decode_wide_kernel<BC>), grid, dim3(512), 0, stream, a);
+    return hipGetLastError();
+}
+
 template <int D, int BC>
 hipError_t launch_split_nt(const DecodeArgs& a, hipStream_t stream) {
     // Up to 16 heads: 128 KiB of copies in flight per workgroup either way.  With
@@ -1015,6 +1313,9 @@ hipError_t launch_split_nt(const DecodeArgs& a, hipStream_t stream) {
         return launch_split<D, BC, 1, 16, 4, 4>(a, stream);
     }
     if (a.G <= 32) return launch_split<D, BC, 2, 8, 4, 4>(a, stream);
+    if constexpr (D == 128) {
+        if (a.G <= 64 && a.lens == nullptr) return launch_wide<BC>(a, stream);
+    }
     if (a.G <= 64) {
         // few units: pairs, each with four slots per wave (46 -> 37 us at 2 x 64 heads x 32K, 16 splits);
         // many: one workgroup per unit (128 vs 173 us for pairs at 64 x 64 heads x 16K, 8 splits)

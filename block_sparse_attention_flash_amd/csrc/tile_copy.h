@@ -1,5 +1,5 @@
-// Address arithmetic of the whole-tile HBM -> LDS copies of the prefill
-// kernels (global_load_lds_dwordx4 with a wave-uniform tile base in SGPRs and
+// Address arithmetic of the whole-tile HBM -> LDS copies of the prefill and
+// wide-group decode kernels (global_load_lds_dwordx4 with a wave-uniform tile base in SGPRs and
 // a 32-bit byte offset per lane), kept host-callable so that every lane's
 // address range can be enumerated and checked on the CPU.
 //
@@ -43,6 +43,14 @@ template <int CPR>
 BLASST_HD inline constexpr uint32_t tile_copy_offset(int wave, int cpw, int f, int lane) {
     const int pp = (wave * cpw + f) * 64 + lane;
     return (uint32_t)((pp / CPR) * (16 * CPR) + (((pp % CPR) ^ chunk_swizzle<CPR>(pp / CPR)) << 4));
+}
+
+// The same for the decode kernels' swizzle, chunk x of tile row r at
+// x ^ (r mod CPR) (the wide-group decode kernel's K and V blocks).
+template <int CPR>
+BLASST_HD inline constexpr uint32_t tile_copy_offset_rowxor(int wave, int cpw, int f, int lane) {
+    const int pp = (wave * cpw + f) * 64 + lane;
+    return (uint32_t)((pp / CPR) * (16 * CPR) + (((pp % CPR) ^ ((pp / CPR) & (CPR - 1))) << 4));
 }
 
 // Tile j of a sequence of T rows runs past its end.

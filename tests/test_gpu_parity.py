@@ -53,6 +53,11 @@ DECODE_SMALL = [
     (4, 16, 4, 5000, 64, 64, 20, 0.02, 64),    # 320 units, d = Bc = 64, ragged N
     (3, 8, 8, 3000, 128, 64, 12, 0.02, 0),     # 288 units, MHA, d = 128 with Bc = 64
     (6, 16, 4, 3000, 64, 128, 12, 0.02, 0),    # 288 units, d = 64 with Bc = 128
+    # 33..64 heads at d = 128: the wide-group kernel (one 8-wave workgroup per split)
+    (33, 64, 1, 600, 128, 128, 4, 0.02, 0),    # 132 units, ragged N (4.7 blocks), splits of 1-2 blocks
+    (2, 48, 1, 3000, 128, 64, 5, 0.02, 64),    # G = 48: the fourth head tile empty; Bc = 64
+    (4, 64, 2, 2000, 128, 128, 16, 0.02, 0),   # S = nk = 16: one block per split (one phase, no K ahead)
+    (3, 40, 1, 5000, 128, 64, 3, 0.02, 128),   # G = 40: a half-filled head tile; 26 blocks per split
 ]
 
 
