@@ -636,12 +636,14 @@ __global__ __launch_bounds__(512) void decode_wide_kernel(DecodeArgs a) {
 
     // block j of K or V -> a tile: copy f of this wave moves 16 bytes per lane (a
     // fixed byte offset inside the block, chunk x of tile row r landing at
-    // x ^ (r mod CPR)) from a wave-uniform block base in SGPRs; only a last block
-    // running past the context re-reads key N - 1 in place of the missing rows
-    // (their scores are masked)
+    // x ^ chunk_swizzle(r), the prefill tiles' map: free of bank conflicts for the
+    // K row reads (16 rows x one chunk per 16 lanes) and the transposed V reads
+    // (4 rows x two chunks per 16 lanes)) from a wave-uniform block base in SGPRs;
+    // only a last block running past the context re-reads key N - 1 in place of
+    // the missing rows (their scores are masked)
     uint32_t toff[CPW];
 #pragma unroll
-    for (int f = 0; f < CPW; ++f) toff[f] = tile_copy_offset_rowxor<CPR>(wave, CPW, f, lane);
+    for (int f = 0; f < CPW; ++f) toff[f] = tile_copy_offset<CPR>(wave, CPW, f, lane);
     auto issue = [&](const uint16_t* base, char* tile, int j) {
         const uint16_t* tbase = base + (size_t)j * BC * D;
         if (__builtin_expect(tile_is_ragged<BC>(j, N), 0)) {
@@ -675,7 +677,7 @@ __global__ __launch_bounds__(512) void decode_wide_kernel(DecodeArgs a) {
 #pragma unroll
                 for (int s = 0; s < DS; ++s) {
                     const int r = 16 * kt + n, c = 4 * s + g;
-                    kf[kt][s] = *(const u32x4*)(kt_base + r * ROWB + ((c ^ (r & (CPR - 1))) << 4));
+                    kf[kt][s] = *(const u32x4*)(kt_base + r * ROWB + ((c ^ chunk_swizzle<CPR>(r)) << 4));
                 }
             const bool tail = tile_is_ragged<BC>(jj, N);  // keys past the context are masked
 #pragma unroll
@@ -794,8 +796,9 @@ __global__ __launch_bounds__(512) void decode_wide_kernel(DecodeArgs a) {
                 const char* vs = vt + u * 32 * ROWB;
                 const int cc = 2 * wave + ((n & 3) >> 1);
                 const int r0 = 4 * g + (n >> 2), r1 = 16 + 4 * g + (n >> 2);
-                const u32x2 lo = lds_read_tr16((const lds_char*)(vs + r0 * ROWB + ((cc ^ (r0 & (CPR - 1))) << 4) + (n & 1) * 8));
-                const u32x2 hi = lds_read_tr16((const lds_char*)(vs + r1 * ROWB + ((cc ^ (r1 & (CPR - 1))) << 4) + (n & 1) * 8));
+                const int sw = chunk_swizzle<CPR>(r0) << 4;  // rows r0 and r0 + 16 share it
+                const u32x2 lo = lds_read_tr16((const lds_char*)(vs + r0 * ROWB + ((cc << 4) ^ sw) + (n & 1) * 8));
+                const u32x2 hi = lds_read_tr16((const lds_char*)(vs + r1 * ROWB + ((cc << 4) ^ sw) + (n & 1) * 8));
                 const bf16x8 av = as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y});
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {

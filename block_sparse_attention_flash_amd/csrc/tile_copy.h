@@ -45,14 +45,6 @@ BLASST_HD inline constexpr uint32_t tile_copy_offset(int wave, int cpw, int f, i
     return (uint32_t)((pp / CPR) * (16 * CPR) + (((pp % CPR) ^ chunk_swizzle<CPR>(pp / CPR)) << 4));
 }
 
-// The same for the decode kernels' swizzle, chunk x of tile row r at
-// x ^ (r mod CPR) (the wide-group decode kernel's K and V blocks).
-template <int CPR>
-BLASST_HD inline constexpr uint32_t tile_copy_offset_rowxor(int wave, int cpw, int f, int lane) {
-    const int pp = (wave * cpw + f) * 64 + lane;
-    return (uint32_t)((pp / CPR) * (16 * CPR) + (((pp % CPR) ^ ((pp / CPR) & (CPR - 1))) << 4));
-}
-
 // Tile j of a sequence of T rows runs past its end.
 template <int BC>
 BLASST_HD inline constexpr bool tile_is_ragged(int j, int T) {

@@ -1,6 +1,6 @@
 // Host check of the prefill and wide-group decode kernels' whole-tile HBM -> LDS
 // copies (global_load_lds_dwordx4 with an SGPR tile base and a 32-bit lane offset):
-// for every supported (d, Bc), wave count, swizzle and sequence length, every lane of
+// for every supported (d, Bc), wave count and sequence length, every lane of
 // every copy of every tile is enumerated through the offset functions the
 // kernels themselves call (csrc/tile_copy.h), and
 //   * the 16 bytes it reads lie inside the sequence's rows [0, T) of the
@@ -32,8 +32,7 @@ static int g_fail = 0;
         }                                                  \
     } while (0)
 
-// ROWXOR: the decode kernels' swizzle (chunk x of row r at x ^ (r mod CPR)), else chunk_swizzle
-template <int D, int BC, bool ROWXOR = false>
+template <int D, int BC>
 void check_config(int NW, const std::vector<int>& lengths) {
     constexpr int CPR = D / 8, ROWB = 2 * D, TILE = BC * ROWB;
     if (TILE % (1024 * NW) != 0) return;
@@ -46,8 +45,7 @@ void check_config(int NW, const std::vector<int>& lengths) {
             for (int wave = 0; wave < NW; ++wave)
                 for (int f = 0; f < CPW; ++f)
                     for (int lane = 0; lane < 64; ++lane) {
-                        const uint32_t off0 = ROWXOR ? tile_copy_offset_rowxor<CPR>(wave, CPW, f, lane)
-                                                     : tile_copy_offset<CPR>(wave, CPW, f, lane);
+                        const uint32_t off0 = tile_copy_offset<CPR>(wave, CPW, f, lane);
                         const uint32_t off = ragged ? tile_copy_clamp<CPR, BC>(off0, j, T) : off0;
                         ++g_checked;
                         CHECK(off % 16 == 0, "misaligned offset %u", off);
@@ -62,8 +60,7 @@ void check_config(int NW, const std::vector<int>& lengths) {
                               lds + 16, TILE);
                         // the LDS position the kernels read logical chunk c of tile row r from
                         const int r = (int)(off0 / ROWB), c = (int)((off0 % ROWB) / 16);
-                        const int sw = ROWXOR ? (r & (CPR - 1)) : chunk_swizzle<CPR>(r);
-                        CHECK(lds == r * ROWB + ((c ^ sw) << 4),
+                        CHECK(lds == r * ROWB + ((c ^ chunk_swizzle<CPR>(r)) << 4),
                               "tile row %d chunk %d lands at LDS %d", r, c, lds);
                         if (row - (long)j * BC == r) hits[(size_t)r * CPR + c] += 1;
                         else CHECK(ragged && row == T - 1, "row %ld re-read outside a ragged tile", row);
@@ -87,8 +84,8 @@ int main() {
         check_config<128, 128>(4 * hpw, lengths);
     }
     // the wide-group decode kernel: eight waves, d = 128, K and V blocks of Bc = 64 or 128 keys
-    check_config<128, 64, true>(8, lengths);
-    check_config<128, 128, true>(8, lengths);
+    check_config<128, 64>(8, lengths);
+    check_config<128, 128>(8, lengths);
     printf("%s: %ld lane copies checked, %d failures\n", g_fail ? "FAILED" : "OK", g_checked, g_fail);
     return g_fail ? 1 : 0;
 }

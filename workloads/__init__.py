@@ -116,7 +116,7 @@ CONFIGS = {
                                 seed=_seed(4), num_splits=32),
     "decode_mqa_16k": Workload("decode_mqa_16k", "decode", B=64, Hq=64, Hkv=1, d=128, T=16384,
                                Bc=128, lambdas=(1e-3,), hot_rate=0.02, seed=_seed(5),
-                               num_splits=8),
+                               num_splits=4),  # 64 x 4 splits: one workgroup per CU
 }
 
 # MLA decode (DeepSeek-V3-like absorbed attention: 128 heads over 512 latent +
