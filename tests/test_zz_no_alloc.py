@@ -6,7 +6,9 @@ caller-owned workspace): the outputs and masks must be equal bit for bit (the
 same kernels), and the merged output must match the FP64 oracle within the
 parity tolerances.  The second call must not change the free device memory,
 and a call whose partials exceed the library's per-GPU array is rejected
-before anything runs.
+before anything runs.  Every decode launch shape (4-wave and paired 16-head
+workgroups, 32 heads, paired 64-head workgroups, head parts, the wide-group
+kernel, up to 40 splits) is also run twice in a row through the array.
 """
 import ctypes
 import sys
@@ -78,6 +80,24 @@ def test_noalloc_two_calls_second_smaller():
     run_both((1, 32, 8, 32768, 128, 128, 16, 1e-3, 1501))
     free0, free1 = run_both((2, 8, 2, 3000, 64, 64, 3, 1e-1, 1502))
     assert free1 == free0
+
+
+MERGE_SHAPES = [
+    # B, Hq, Hkv, N, d, Bc, S, lambda, seed
+    (4, 16, 4, 5000, 64, 64, 20, 1e-3, 1601),    # 320 units, 16 heads: 4-wave workgroups
+    (2, 64, 2, 3000, 128, 128, 5, 1e-3, 1602),   # 32 heads
+    (2, 64, 1, 3000, 64, 128, 5, 1e-1, 1603),    # 64 heads at d = 64: paired 64-head workgroups
+    (1, 128, 1, 3000, 128, 128, 4, 1e-3, 1604),  # 128 heads: two head parts per split
+    (2, 8, 2, 9000, 64, 64, 32, 0.5, 1605),      # 32 splits
+    (3, 8, 8, 3000, 128, 64, 40, 1e-3, 1606),    # 40 splits (the merge's loop form)
+    (8, 64, 1, 2000, 128, 128, 4, 1e-3, 1607),   # 64 heads at d = 128: the wide-group kernel
+]
+
+
+@pytest.mark.parametrize("shape", MERGE_SHAPES, ids=lambda s: "B%d_Hq%d_Hkv%d_N%d_d%d_Bc%d_S%d" % s[:7])
+def test_noalloc_merge_paths_twice(shape):
+    run_both(shape)
+    run_both(shape)
 
 
 def test_noalloc_rejects_partials_beyond_the_array():
