@@ -591,6 +591,12 @@ __global__ __launch_bounds__(512) void decode_wide_kernel(DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) char lds_v[2][TILE];
     __shared__ __attribute__((aligned(16))) char lds_p[KG * 64 * 64];  // [unit][head][32 keys] bf16
     __shared__ float lds_pmax[KG][64];
+    // decision bytes of up to 32 blocks, written to HBM a chunk at a time with consecutive lanes
+    // on consecutive bytes of a head's row (one byte store per decision would cost a memory
+    // transaction each)
+    constexpr int MCH = 32;
+    __shared__ uint8_t lds_mask[MCH][64];
+    __shared__ uint8_t lds_vmask[MCH];
     float(*lds_l)[64] = (float(*)[64])lds_p;  // [W][64] after the last step
 
     const int split = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
@@ -730,14 +736,11 @@ __global__ __launch_bounds__(512) void decode_wide_kernel(DecodeArgs a) {
             }
             vkeep = __any(keepm != 0u);
             lag = __any(lag);  // the same in every wave: the same lanes hold the same maxima
-            if (a.skip != nullptr && wave == 0 && g == 0) {
+            if (wave == 0 && g == 0) {
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt)
-                    if (head_ok[nt])
-                        a.skip[((size_t)b * a.Hq + (size_t)hkv * G + nt * 16 + n) * nk + jj] =
-                            (uint8_t)(((keepm >> nt) & 1u) ^ 1u);
+                for (int nt = 0; nt < NT; ++nt) lds_mask[(jj - j0) % MCH][nt * 16 + n] = (uint8_t)(((keepm >> nt) & 1u) ^ 1u);
+                if (n == 0) lds_vmask[(jj - j0) % MCH] = (uint8_t)!vkeep;
             }
-            if (a.vskip != nullptr && threadIdx.x == 0) a.vskip[((size_t)b * a.Hkv + hkv) * nk + jj] = (uint8_t)!vkeep;
             // K(jj + 2) into the slot K(jj) used, then V(jj) (kept blocks only)
             if (jj + 2 < j1) {
                 issue(kbase, lds_k[x], jj + 2);
@@ -787,6 +790,20 @@ __global__ __launch_bounds__(512) void decode_wide_kernel(DecodeArgs a) {
         // V(jj - 1) and K(jj + 1) (issued last step) have landed; only this step's copies may be in flight
         wait_vm<CPW>(nissued);
         __syncthreads();  // P and V of block jj - 1 and K(jj + 1) visible to every wave
+
+        // ---- a full chunk of decision bytes (or the split's last) to HBM; the chunk's bytes are
+        //      rewritten only after the next step's first barrier, when every wave has read them
+        if (front && ((jj - j0) % MCH == MCH - 1 || jj == j1 - 1)) {
+            const int base = jj - (jj - j0) % MCH, cnt = (jj - j0) % MCH + 1;
+            if (a.skip != nullptr) {
+                for (int t = threadIdx.x; t < G * MCH; t += 64 * W) {
+                    const int h = t / MCH, c = t % MCH;
+                    if (c < cnt) a.skip[((size_t)b * a.Hq + (size_t)hkv * G + h) * nk + base + c] = lds_mask[c][h];
+                }
+            }
+            if (a.vskip != nullptr && threadIdx.x < cnt)
+                a.vskip[((size_t)b * a.Hkv + hkv) * nk + base + threadIdx.x] = lds_vmask[threadIdx.x];
+        }
 
         // ---- O^T rows 16 wave .. + 15 += V^T P^T over block jj - 1's units
         if (vkeep_prev) {
