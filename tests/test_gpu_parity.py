@@ -58,6 +58,8 @@ DECODE_SMALL = [
     (2, 48, 1, 3000, 128, 64, 5, 0.02, 64),    # G = 48: the fourth head tile empty; Bc = 64
     (4, 64, 2, 2000, 128, 128, 16, 0.02, 0),   # S = nk = 16: one block per split (one phase, no K ahead)
     (3, 40, 1, 5000, 128, 64, 3, 0.02, 128),   # G = 40: a half-filled head tile; 26 blocks per split
+    (1, 64, 1, 9000, 128, 128, 1, 0.02, 256),  # one split of 71 blocks: decision bytes in chunks of 32, 32, 7
+    (2, 56, 1, 8200, 128, 64, 2, 0.02, 0),     # G = 56, Bc = 64: 64 and 65 blocks per split (a 1-block chunk)
 ]
 
 
