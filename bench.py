@@ -87,15 +87,16 @@ def parse():
     p.add_argument("--no-other-configs", action="store_true",
                    help="skip the other workload configurations and the ragged batches")
     p.add_argument("--no-length-sweep-timing", action="store_true",
-                   help="skip the decode timing of the 128K length-sweep sequences at lambda = a/L")
+                   help="skip the decode and prefill timing of the 128K length-sweep sequences at lambda = a/L")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--profile-target", choices=["decode", "decode_mqa", "decode_dense", "decode_ceiling",
-                                                 "decode_sweep128", "prefill", "copy"], default=None,
+                                                 "decode_sweep128", "prefill", "prefill_sweep128", "copy"],
+                   default=None,
                    help="run only one kernel a few times (for hardware-counter collection) and exit")
     p.add_argument("--profile-lambda", type=float, default=None,
-                   help="lambda for --profile-target decode / decode_mqa (default: the workload's) and "
-                        "decode_sweep128 (default 0)")
+                   help="lambda for --profile-target decode / decode_mqa / prefill (default: the workload's) and "
+                        "decode_sweep128 / prefill_sweep128 (default 0)")
     p.add_argument("--profile-launches", type=int, default=10)
     p.add_argument("--length-sweep", action="store_true",
                    help="instead of the bench: sparsity drift over 4K-128K context and the lambda = a/L calibration")
@@ -166,7 +167,12 @@ def profile_target(args, lib, torch, W):
                                        by["split"] - by["k"] - by["v_kept"] - B * Hq * d * 2,
                                        float(vskip.cpu().numpy().mean())))
         return
-    w = W.CONFIGS["prefill_32k"]
+    if args.profile_target == "prefill_sweep128":
+        w = W.sweep_workload("prefill", W.SWEEP_LENGTHS[-1], "evaluation")
+        lam = args.profile_lambda or 0.0
+    else:
+        w = W.CONFIGS["prefill_32k"]
+        lam = 1e-3 if args.profile_lambda is None else args.profile_lambda
     x = {k: dev(v) for k, v in W.generate(w).items()}
     B, Hq, T, d, Bc = w.B, w.Hq, w.T, w.d, w.Bc
     nq = -(-T // Bc)
@@ -177,9 +183,11 @@ def profile_target(args, lib, torch, W):
     P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
     for _ in range(n):
         assert lib.blasst_prefill(P(x["q"]), P(x["k"]), P(x["v"]), P(o), P(lse), P(mask), B, Hq, T, d, w.G, Bc,
-                                  ctypes.c_double(1e-3), 1, sp) == 0
+                                  ctypes.c_double(lam), 1, sp) == 0
     torch.cuda.synchronize()
-    print("prefill_32k: %d launches at lambda=1e-3" % n)
+    visited = B * Hq * nq * (nq + 1) // 2
+    print("%s: %d launches at lambda=%g, block sparsity %.4f" % (w.name, n, lam,
+                                                                 float((mask == 1).sum().item()) / visited))
 
 
 SWEEP_LAMBDAS = tuple(float(x) for x in np.geomspace(1e-5, 0.9, 50))  # candidate thresholds
@@ -689,7 +697,14 @@ def bench_decode_length_sweep(args, lib, torch, W, bsa):
     dense_ms = trials(lambda: ok(lib.blasst_decode_dense(P(x["q"]), P(x["k"]), P(x["v"]), P(o_part), P(lse_part),
                                                           B, Hq, N, d, w.G, Bc, S, sp)))
     targets = {"a/L, 50%": policy.lambda_for(0.5, L, alpha, beta), "a/L, 70%": policy.lambda_for(0.7, L, alpha, beta)}
-    points = [("lambda = 0", 0.0), ("fixed 1e-3", 1e-3), ("fixed 3e-3", 3e-3)] + list(targets.items())
+    # sparsity-matched points: lambda read off these sequences' own margins (block sparsity 50%, and the
+    # 73.2% at which the blog quotes its decode speed-up)
+    own, _ = bsa.decode_margins(x["q"], x["k"], S, Bc=Bc)
+    matched = {"matched 50%": policy.lambda_at_sparsity(own, 0.5),
+               "matched 73.2%": policy.lambda_at_sparsity(own, 0.732)}
+    del own
+    points = [("lambda = 0", 0.0), ("fixed 1e-3", 1e-3), ("fixed 3e-3", 3e-3)] + list(targets.items()) + \
+        list(matched.items())
     dense_bytes = decode_bytes(w, np.zeros((B, w.Hkv, nk), np.uint8))["split"]
     rows = []
     for label, lam in points:
@@ -716,6 +731,88 @@ def bench_decode_length_sweep(args, lib, torch, W, bsa):
                 policy={"alpha": alpha, "beta": beta, "points": npts, "calibration_lengths": list(W.SWEEP_LENGTHS[:5]),
                         "calibration_splits": SWEEP128_SPLITS},
                 dense_kernel_us=round(dense_ms[0] * 1e3, 2), by_lambda=rows)
+
+
+def bench_prefill_length_sweep(args, lib, torch, W, bsa):
+    """What a prefill skip buys where skipping is common: the length-sweep family's held-out 128K causal
+    sequence (B = 1, Hq = 32, Hkv = 8, d = 128, Bc = 128) through blasst_prefill at lambda = a/L for 50% and
+    70% target sparsity (a fitted on the prefill margins of the 4K-64K calibration sequences) and at fixed
+    lambdas, against lambda = 0 and the kernel built without the skip test.  A skipped tile still costs
+    its S = Q K^T product and row maxima; only the exponentials and P V are saved, so at block sparsity s
+    the executed FLOPs fall to (1 - s/2) of the dense count."""
+    from block_sparse_attention_flash_amd import policy
+    lengths = W.SWEEP_LENGTHS[:5]
+    margins = [sweep_margins("prefill", L, "calibration", W, bsa)[0] for L in lengths]
+    a_pts, s_pts = policy.calibration_points(margins, list(lengths), SWEEP_LAMBDAS)
+    alpha, beta = policy.fit_exponential(a_pts, s_pts)
+    del margins
+    L = W.SWEEP_LENGTHS[-1]
+    w = W.sweep_workload("prefill", L, "evaluation")
+    x = {k: dev(v) for k, v in W.generate(w).items()}
+    B, Hq, T, d, Bc = w.B, w.Hq, w.T, w.d, w.Bc
+    nq = -(-T // Bc)
+    o = torch.empty((B, Hq, T, d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device="cuda")
+    mask = torch.empty((B, Hq, nq, nq), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    visited = B * Hq * nq * (nq + 1) // 2
+    tile_flops = 2.0 * Bc * Bc * d
+
+    def ok(st):
+        if st != 0:
+            raise RuntimeError("libblasst call failed with status %d" % st)
+
+    def trials(fn, reps=2):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(TRIALS):
+            s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s0.record(stream)
+            for _ in range(reps):
+                fn()
+            s1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(s0.elapsed_time(s1) / reps)
+        return float(np.median(ts)), min(ts), max(ts)
+
+    no_test_ms = trials(lambda: ok(lib.blasst_prefill_dense(P(x["q"]), P(x["k"]), P(x["v"]), P(o), P(lse),
+                                                            B, Hq, T, d, w.G, Bc, 1, sp)))
+    targets = {"a/L, 50%": policy.lambda_for(0.5, L, alpha, beta), "a/L, 70%": policy.lambda_for(0.7, L, alpha, beta)}
+    # sparsity-matched points: lambda read off this sequence's own margins (block sparsity 50%, and the
+    # 71.9% at which the blog quotes its prefill speed-up)
+    own = bsa.prefill_margins(x["q"], x["k"], Bc=Bc, causal=True)
+    matched = {"matched 50%": policy.lambda_at_sparsity(own, 0.5),
+               "matched 71.9%": policy.lambda_at_sparsity(own, 0.719)}
+    del own
+    points = [("lambda = 0", 0.0), ("fixed 1e-3", 1e-3), ("fixed 3e-3", 3e-3)] + list(targets.items()) + \
+        list(matched.items())
+    rows = []
+    for label, lam in points:
+        a = (P(x["q"]), P(x["k"]), P(x["v"]), P(o), P(lse), P(mask), B, Hq, T, d, w.G, Bc,
+             ctypes.c_double(lam), 1, sp)
+        ms = trials(lambda: ok(lib.blasst_prefill(*a)))
+        torch.cuda.synchronize()
+        skipped = int((mask == 1).sum().item())
+        kept = visited - skipped
+        flops = (visited + kept) * tile_flops
+        rows.append(dict(point=label, lam=lam, ms=round(ms[0], 3), ms_min=round(ms[1], 3), ms_max=round(ms[2], 3),
+                         block_sparsity=round(skipped / visited, 4),
+                         executed_tflop=round(flops / 1e12, 2),
+                         tflops_executed=round(flops / (ms[0] * 1e-3) / 1e12, 1),
+                         frac_of_mfma_peak=round(flops / (ms[0] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                         speedup_vs_no_test_kernel=round(no_test_ms[0] / ms[0], 4),
+                         flops_ratio_dense_over_this=round(2 * visited / (visited + kept), 4)))
+    l0 = rows[0]["ms"]
+    for r in rows:
+        r["speedup_vs_lambda0"] = round(l0 / r["ms"], 4)
+    del x, o, lse, mask
+    torch.cuda.empty_cache()
+    return dict(workload=w.name, B=B, Hq=Hq, Hkv=w.Hkv, d=d, context=T, Bc=Bc, causal=True,
+                policy={"alpha": alpha, "beta": beta, "points": int(len(a_pts)), "calibration_lengths": list(lengths)},
+                no_skip_test_kernel_ms=round(no_test_ms[0], 3), by_lambda=rows)
 
 
 def bench_mla(args, lib, torch, W):
@@ -871,6 +968,7 @@ def main():
             torch.cuda.empty_cache()
         configs["ragged"] = bench_ragged(args, lib, torch, W)
     sweep128 = None if args.no_length_sweep_timing else bench_decode_length_sweep(args, lib, torch, W, bsa)
+    psweep128 = None if args.no_length_sweep_timing else bench_prefill_length_sweep(args, lib, torch, W, bsa)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args, d)
 
     by = d["bytes"]
@@ -920,6 +1018,7 @@ def main():
         "mla_decode": mla,
         "other_configs": configs,
         "decode_length_sweep_128k": sweep128,
+        "prefill_length_sweep_128k": psweep128,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -37,6 +37,7 @@ struct PrefillArgs {
     float* margin = nullptr;  // margin pass only: [B, Hq, nq, nk]
     const int* lens = nullptr;  // ragged batch: [B] sequence lengths (device), clamped to [0, T]; T, nq = capacity
     bool dense = false;         // the kernel built without the skip test (every tile kept)
+    int xcd_rot = 1 << 30;      // query blocks per turn of the kv-group -> XCD rotation (set at launch)
 };
 
 // MLA decode (absorbed latent form): 576-wide cache rows, value = the first 512 columns, Bc in {32, 64}.

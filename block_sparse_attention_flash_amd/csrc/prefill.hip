@@ -13,7 +13,9 @@
 // one tile copy feeds HPW times the MFMA work.  Workgroups are issued heaviest
 // first (the last query block has the most KV tiles under the causal mask), and
 // the workgroups of one query block are spread so that those sharing a kv head
-// land on the same XCD (its L2 then serves their common K/V tiles).
+// land on the same XCD (its L2 then serves their common K/V tiles); which kv
+// heads an XCD serves turns every few query blocks, so that heads that skip
+// less than the others do not keep one XCD busy after the rest.
 //
 // Per KV tile (all on MFMA 32x32x16 bf16, fp32 accumulate):
 //   S^T = K Q^T      A = K rows from LDS (ds_read_b128), B = Q^T in registers.
@@ -30,6 +32,9 @@
 // stages deep, XOR-swizzled by 16-byte chunk so both the row reads and the
 // transposed reads are bank-conflict free.  Only the diagonal tile (and a ragged
 // last tile) pays for causal / tail masking.
+#include <algorithm>
+#include <atomic>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -119,18 +124,23 @@ __global__ __launch_bounds__(2 * BC * HPW) void prefill_kernel(PrefillArgs a) {
         int bh = L % bh_count;
         // Workgroups go round-robin over the 8 XCDs; the head groups of a kv group
         // are kept on one XCD, whose L2 then serves their common K/V tiles.  A plain
-        // batch gives each XCD a contiguous range of (sequence, head group); a ragged
-        // one (more than 64 sequences, with a multiple of 8 kv groups) gives XCD x
-        // kv groups x, x + 8, ..., so every sequence's work is spread over all eight
-        // XCDs (whole sequences per XCD ran a 16K sequence among three empty ones on a
-        // quarter of the chip).
+        // batch gives each XCD one eighth of the (sequence, head group) pairs, and
+        // which eighth turns every xcd_rot query blocks (about the query blocks one
+        // XCD holds at once): heads skip at very different rates, and with a fixed
+        // eighth the XCD holding the least-skipping heads set the launch time (up to
+        // 1.16x the mean XCD's work at 50% sparsity on the 32K length sweep).  A
+        // ragged batch (more than 64 sequences, with a multiple of 8 kv groups) gives
+        // XCD x kv groups x, x + 8, ..., so every sequence's work is spread over all
+        // eight XCDs (whole sequences per XCD ran a 16K sequence among three empty ones
+        // on a quarter of the chip).
         const int hgpk = a.G / HPW;            // head groups per kv group
         const int nkvg = bh_count / hgpk;      // kv groups in the batch
         if (a.lens && nkvg % 8 == 0) {
             const int x = bh % 8, s = bh / 8;
             bh = (x + 8 * (s / hgpk)) * hgpk + s % hgpk;
         } else if (bh_count % 8 == 0) {
-            bh = (bh % 8) * (bh_count / 8) + bh / 8;
+            const int turn = (L / bh_count) / a.xcd_rot;
+            bh = ((bh % 8 + turn) % 8) * (bh_count / 8) + bh / 8;
         }
         hgrp = bh % hg_count;
         b = bh / hg_count;
@@ -439,8 +449,38 @@ __global__ __launch_bounds__(2 * BC * HPW) void prefill_kernel(PrefillArgs a) {
         for (int j = jend + lane; j < a.nk; j += 64) mask_row[j] = 2;
 }
 
+// Workgroups of prefill_kernel<D, BC, HPW> resident on the whole device at once
+// (compute units x workgroups per unit), queried once per device.
 template <int D, int BC, int HPW>
-hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
+hipError_t resident_workgroups(int* out) {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cache[kMaxDevices];
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        int cus = 0, per_cu = 0;
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, prefill_kernel<D, BC, HPW, true>, 2 * BC * HPW, 0);
+        if (e != hipSuccess) return e;
+        n = std::max(1, cus) * std::max(1, per_cu);
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    *out = n;
+    return hipSuccess;
+}
+
+template <int D, int BC, int HPW>
+hipError_t launch(const PrefillArgs& a_in, hipStream_t stream) {
+    PrefillArgs a = a_in;
+    int resident = 0;
+    hipError_t e = resident_workgroups<D, BC, HPW>(&resident);
+    if (e != hipSuccess) return e;
+    // one turn of the kv-group -> XCD rotation per batch of resident workgroups
+    a.xcd_rot = std::max(1, resident / std::max(1, a.B * (a.Hq / HPW)));
     const dim3 grid((unsigned)a.nq * a.B * (a.Hq / HPW));
     if (a.dense)
         hipLaunchKernelGGL((prefill_kernel<D, BC, HPW, false>), grid, dim3(2 * BC * HPW), 0, stream, a);

@@ -93,3 +93,28 @@ def lambda_for(target_sparsity: float, length: int, alpha: float, beta: float) -
     if not (0.0 <= target_sparsity <= 1.0) or length <= 0:
         raise ValueError("target sparsity in [0, 1] and a positive length")
     return min(alpha * math.exp(beta * target_sparsity) / length, math.nextafter(1.0, 0.0))
+
+
+def lambda_at_sparsity(margins, target_sparsity: float) -> float:
+    """The inverse of sparsity_at on one set of margins: a lambda at which the
+    fraction of decisions skipped is the target rounded up to a whole decision
+    (k = ceil(target * n) decisions, more where the k-th smallest margin is
+    tied).  ln(lambda) lies above the k-th smallest margin and at most at the
+    next one.  Used to time a kernel at a stated sparsity; clipped below 1
+    (decisions with margin 0, the blocks that set the running max, are never
+    skipped) and above 0 (lambda = 0 never skips)."""
+    if not (0.0 <= target_sparsity <= 1.0):
+        raise ValueError("target sparsity in [0, 1]")
+    m = _as_numpy(margins).ravel()
+    m = np.sort(m[~np.isnan(m)])
+    k = int(math.ceil(target_sparsity * m.size))
+    if k == 0:
+        return 0.0
+    lo = float(m[k - 1])
+    hi = float(m[k]) if k < m.size else 0.0
+    if hi > lo:
+        ln_lam = 0.5 * (lo + hi) if math.isfinite(lo) else hi - 1.0
+    else:
+        ln_lam = math.nextafter(lo, math.inf) if math.isfinite(lo) else -700.0
+    lam = math.exp(ln_lam) if ln_lam < 0.0 else 1.0
+    return min(max(lam, math.ulp(0.0)), math.nextafter(1.0, 0.0))

@@ -151,3 +151,29 @@ def test_calibration_points_pairs_lambda_times_length_with_sparsity():
     assert list(a) == [1.0, 10.0, 4.0, 40.0]
     np.testing.assert_array_equal(s[:2], policy.sparsity_at(margins[0], lams))
     np.testing.assert_array_equal(s[2:], policy.sparsity_at(margins[1], lams))
+
+
+def test_lambda_at_sparsity_inverts_sparsity_at():
+    rng = np.random.default_rng(11)
+    m = rng.normal(-6.0, 3.0, size=4001)
+    m = np.minimum(m, 0.0)
+    m[:5] = -np.inf   # blocks no row of which sees a key: skipped at any lambda > 0
+    m[5:9] = np.nan   # not visited
+    m[9:40] = 0.0     # blocks that set the running max: never skipped below lambda = 1
+    n = np.count_nonzero(~np.isnan(m))
+    for target in (0.0, 1e-4, 0.1, 0.5, 0.719, 0.9):
+        lam = policy.lambda_at_sparsity(m, target)
+        assert 0.0 <= lam < 1.0
+        got = round(policy.sparsity_at(m, [lam])[0] * n)
+        k = math.ceil(target * n)
+        flat = np.sort(m[~np.isnan(m)])
+        want = 0 if k == 0 else int(np.count_nonzero(flat <= flat[k - 1]))  # k, or the whole tie group
+        assert got == want, (target, got, want)
+    # ties: the whole tie group is skipped
+    t = np.array([-3.0, -2.0, -2.0, -2.0, -1.0])
+    assert policy.sparsity_at(t, [policy.lambda_at_sparsity(t, 0.4)])[0] == 0.8
+    # only -inf below the target: any lambda > 0 skips exactly those
+    t = np.array([-np.inf, -np.inf, -1.0, 0.0])
+    assert policy.sparsity_at(t, [policy.lambda_at_sparsity(t, 0.5)])[0] == 0.5
+    # a target past the margin-0 decisions stops at them
+    assert policy.sparsity_at(m, [policy.lambda_at_sparsity(m, 1.0)])[0] == np.count_nonzero(m < 0.0) / n
