@@ -102,6 +102,12 @@ __global__ __launch_bounds__(2 * BC * HPW) void prefill_kernel(PrefillArgs a) {
             i = lo;
             const int r = L - items_from(i + 1);
             hgrp = r % hg_count;
+            if (hg_count % 8 == 0) {
+                // XCD r % 8 serves head groups of one residue mod 8; the residue turns
+                // every xcd_rot query blocks, as for a plain batch (below)
+                const int turn = (a.nq - 1 - i) / a.xcd_rot;
+                hgrp = (hgrp % 8 + turn) % 8 + 8 * (hgrp / 8);
+            }
             uint64_t has = __ballot(nqb > i);
             for (int k = r / hg_count; k > 0; --k) has &= has - 1;
             b = min(__builtin_ctzll(has), a.B - 1);

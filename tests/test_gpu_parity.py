@@ -81,6 +81,9 @@ PREFILL_SMALL = [
     (2, 2, 2, 300, 64, 128, 0.03),
     (1, 8, 2, 513, 128, 64, 0.02),
     (1, 1, 1, 50, 64, 64, 0.05),       # T < Bc
+    # 16 (sequence, head group) pairs over 21 query blocks: on a 256-CU device 16 blocks are resident
+    # at once, so the kv-group -> XCD map turns once
+    (2, 16, 4, 2600, 128, 128, 0.02),
 ]
 
 

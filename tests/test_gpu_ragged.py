@@ -67,6 +67,8 @@ PREFILL = [
     (4, 4, 2, 700, 64, 64, [700, 0, 65, 300]),
     (3, 4, 1, 513, 128, 128, [1, 513, 256]),
     (2, 2, 2, 300, 128, 64, [299, 64]),
+    # 8 head groups per sequence: the head-group -> XCD map turns once along the 21 query blocks
+    (2, 16, 4, 2600, 128, 128, [2600, 1700]),
     # more than 64 sequences: the kv-group-per-XCD order instead of the in-kernel work list
     (72, 2, 2, 200, 64, 64, [(37 * b) % 201 for b in range(72)]),
 ]
