@@ -69,7 +69,7 @@ __global__ __launch_bounds__(2 * BC * HPW) void prefill_kernel(PrefillArgs a) {
 
     __shared__ __attribute__((aligned(16))) char lds_k[2][TILE];
     __shared__ __attribute__((aligned(16))) char lds_v[2][TILE];
-    __shared__ int lds_vote[NW];
+    __shared__ __attribute__((aligned(16))) uint32_t lds_vote[NW];
 
     // ---- workgroup -> (query block, head group, batch)
     const int hg_count = a.Hq / HPW;
@@ -309,7 +309,7 @@ __global__ __launch_bounds__(2 * BC * HPW) void prefill_kernel(PrefillArgs a) {
         if constexpr (SKIP) {
             const bool vote_skip = !row_ok || mt == kNegInf || (mt - m_new) * c < a.thr;
             const bool wave_skip = __all(vote_skip);
-            if (lane == 0) lds_vote[wave] = wave_skip;
+            if (lane == 0) lds_vote[wave] = wave_skip ? 1u : 0u;
         }
     };
 
@@ -317,8 +317,18 @@ __global__ __launch_bounds__(2 * BC * HPW) void prefill_kernel(PrefillArgs a) {
     auto phase_y = [&](int j) {
         bool skip = SKIP;
         if constexpr (SKIP) {
-#pragma unroll
-            for (int w = 0; w < NWH; ++w) skip = skip && lds_vote[hsub * NWH + w];
+            // the head's NWH votes are adjacent words: one LDS read for all of them (an
+            // AND written with && waited for each word in turn before the next read)
+            static_assert(NWH == 2 || NWH == 4, "votes read as one 8- or 16-byte word");
+            uint32_t all;
+            if constexpr (NWH == 4) {
+                const u32x4 v = *(const u32x4*)&lds_vote[hsub * 4];
+                all = v[0] & v[1] & v[2] & v[3];
+            } else {
+                const u32x2 v = *(const u32x2*)&lds_vote[hsub * 2];
+                all = v[0] & v[1];
+            }
+            skip = __builtin_amdgcn_readfirstlane(all) != 0;
         }
         if (wrow == 0 && lane == 0 && mask_row) mask_row[j] = (uint8_t)skip;
         if (skip) return;
