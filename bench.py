@@ -100,6 +100,9 @@ def parse():
     p.add_argument("--profile-launches", type=int, default=10)
     p.add_argument("--length-sweep", action="store_true",
                    help="instead of the bench: sparsity drift over 4K-128K context and the lambda = a/L calibration")
+    p.add_argument("--speedup-curve", action="store_true",
+                   help="instead of the bench: decode (128K) and causal prefill (32K-128K) kernel speed-up against "
+                        "block sparsity 0-90%%, lambda read off each sequence's own margins")
     return p.parse_args()
 
 
@@ -815,6 +818,102 @@ def bench_prefill_length_sweep(args, lib, torch, W, bsa):
                 no_skip_test_kernel_ms=round(no_test_ms[0], 3), by_lambda=rows)
 
 
+CURVE_TARGETS = (0.0, 0.25, 0.4, 0.5, 0.6, 0.7, 0.8, 0.9)  # block sparsities of the speed-up curve
+
+
+def speedup_curve(args, lib, torch, W, bsa):
+    """Kernel speed-up against block sparsity, the pages' kernel-speed figure re-measured on this GPU:
+    the length-sweep family's evaluation sequences, decoded at 128K (B = 4, 32/8 heads, 4 splits,
+    split kernel) and prefilled causally at 32K, 64K and 128K (B = 1, 32/8 heads).  For each target
+    sparsity lambda is read off the sequence's own decision margins (policy.lambda_at_sparsity); each
+    point gives the kernel time, the sparsity reached, the speed-up over lambda = 0 and the bound the
+    skipped work sets (decode: HBM bytes, all of K always read; prefill: FLOPs, S = Q K^T always
+    formed)."""
+    from block_sparse_attention_flash_amd import policy
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+
+    def ok(st):
+        if st != 0:
+            raise RuntimeError("libblasst call failed with status %d" % st)
+
+    def trials(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(TRIALS):
+            s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s0.record(stream)
+            for _ in range(reps):
+                fn()
+            s1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(s0.elapsed_time(s1) / reps)
+        return float(np.median(ts))
+
+    out = {}
+    # ---- decode, 128K
+    L = W.SWEEP_LENGTHS[-1]
+    w = W.sweep_workload("decode", L, "evaluation").with_(num_splits=SWEEP128_SPLITS)
+    x = {k: dev(v) for k, v in W.generate(w).items()}
+    B, Hq, N, d, Bc, S = w.B, w.Hq, w.T, w.d, w.Bc, w.num_splits
+    nk = -(-N // Bc)
+    o_part = torch.empty((B, Hq, S, d), dtype=torch.float32, device="cuda")
+    lse_part = torch.empty((B, Hq, S), dtype=torch.float32, device="cuda")
+    skip = torch.empty((B, Hq, nk), dtype=torch.uint8, device="cuda")
+    vskip = torch.empty((B, w.Hkv, nk), dtype=torch.uint8, device="cuda")
+    own, _ = bsa.decode_margins(x["q"], x["k"], S, Bc=Bc)
+    dense_us = 1e3 * trials(lambda: ok(lib.blasst_decode_dense(P(x["q"]), P(x["k"]), P(x["v"]), P(o_part),
+                                                               P(lse_part), B, Hq, N, d, w.G, Bc, S, sp)), 20)
+    rows = []
+    for target in CURVE_TARGETS:
+        lam = policy.lambda_at_sparsity(own, target) if target > 0 else 0.0
+        a = (P(x["q"]), P(x["k"]), P(x["v"]), P(o_part), P(lse_part), P(skip), P(vskip), B, Hq, N, d, w.G, Bc,
+             ctypes.c_double(lam), 1, S, sp)
+        us = 1e3 * trials(lambda: ok(lib.blasst_decode(*a)), 20)
+        by = decode_bytes(w, vskip.cpu().numpy())["split"]
+        rows.append(dict(target=target, lam=lam, block_sparsity=round(float(skip.float().mean().item()), 4),
+                         vload_sparsity=round(float(vskip.float().mean().item()), 4), us=round(us, 2),
+                         bytes_per_launch=by))
+    for r in rows:
+        r["speedup_vs_lambda0"] = round(rows[0]["us"] / r["us"], 4)
+        r["speedup_vs_dense_kernel"] = round(dense_us / r["us"], 4)
+        r["bytes_bound"] = round(rows[0]["bytes_per_launch"] / r["bytes_per_launch"], 4)
+    out["decode_%dk" % (L // 1024)] = dict(B=B, Hq=Hq, Hkv=w.Hkv, d=d, context=N, Bc=Bc, num_splits=S,
+                                           dense_kernel_us=round(dense_us, 2), points=rows)
+    del x, o_part, lse_part, skip, vskip, own
+    torch.cuda.empty_cache()
+    # ---- causal prefill, 32K / 64K / 128K
+    for L in W.SWEEP_LENGTHS[3:]:
+        w = W.sweep_workload("prefill", L, "evaluation")
+        x = {k: dev(v) for k, v in W.generate(w).items()}
+        B, Hq, T, d, Bc = w.B, w.Hq, w.T, w.d, w.Bc
+        nq = -(-T // Bc)
+        o = torch.empty((B, Hq, T, d), dtype=torch.float32, device="cuda")
+        lse = torch.empty((B, Hq, T), dtype=torch.float32, device="cuda")
+        mask = torch.empty((B, Hq, nq, nq), dtype=torch.uint8, device="cuda")
+        own = bsa.prefill_margins(x["q"], x["k"], Bc=Bc, causal=True)
+        visited = B * Hq * nq * (nq + 1) // 2
+        reps = max(1, (131072 // T) ** 2 // 4)
+        rows = []
+        for target in CURVE_TARGETS:
+            lam = policy.lambda_at_sparsity(own, target) if target > 0 else 0.0
+            a = (P(x["q"]), P(x["k"]), P(x["v"]), P(o), P(lse), P(mask), B, Hq, T, d, w.G, Bc,
+                 ctypes.c_double(lam), 1, sp)
+            ms = trials(lambda: ok(lib.blasst_prefill(*a)), reps)
+            kept = visited - int((mask == 1).sum().item())
+            rows.append(dict(target=target, lam=lam, block_sparsity=round(1 - kept / visited, 4), ms=round(ms, 3),
+                             flops_bound=round(2 * visited / (visited + kept), 4)))
+        for r in rows:
+            r["speedup_vs_lambda0"] = round(rows[0]["ms"] / r["ms"], 4)
+        out["prefill_%dk" % (L // 1024)] = dict(B=B, Hq=Hq, Hkv=w.Hkv, d=d, context=T, Bc=Bc, causal=True,
+                                                points=rows)
+        del x, o, lse, mask, own
+        torch.cuda.empty_cache()
+    return out
+
+
 def bench_mla(args, lib, torch, W):
     """MLA decode split kernel at 32K context, with 64- and 32-token blocks: time, HBM bytes (the cache
     rows are read once), the executed FLOPs (S for every head and token; P V for the kept blocks of each
@@ -955,6 +1054,9 @@ def main():
         rep = {"decode": length_sweep("decode", W.SWEEP_LENGTHS, W.SWEEP_LENGTHS[:5], W, bsa, log=say),
                "prefill": length_sweep("prefill", W.SWEEP_LENGTHS, W.SWEEP_LENGTHS[:5], W, bsa, log=say)}
         print(json.dumps({"length_sweep": rep}), flush=True)
+        return
+    if args.speedup_curve:
+        print(json.dumps({"speedup_curve": speedup_curve(args, lib, torch, W, bsa)}), flush=True)
         return
 
     d = bench_decode(args, lib, torch, W)
