@@ -437,6 +437,7 @@ def bench_prefill(args, lib, torch, W):
             ts.append(s0.elapsed_time(s1) / args.prefill_reps)
         return float(np.median(ts)), min(ts), max(ts)
 
+    o0 = lse0 = None
     for lam in (0.0,) + tuple(w.lambdas):
         a = (P(x["q"]), P(x["k"]), P(x["v"]), P(o), P(lse), P(mask), B, Hq, T, d, w.G, Bc,
              ctypes.c_double(lam), 1, sp)
@@ -451,6 +452,18 @@ def bench_prefill(args, lib, torch, W):
                                frac_of_mfma_peak=round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                                block_sparsity=round(skipped / visited, 5),
                                executed_tflop=round(flops / 1e12, 4))
+        # the skip's error against the dense (lambda = 0) output of the same kernel, untimed
+        if o0 is None:
+            o0, lse0 = o.clone(), lse.clone()
+        else:
+            diff = (o - o0).view(-1, d)
+            rel = diff.norm(dim=1) / o0.view(-1, d).norm(dim=1).clamp_min(1e-30)
+            out["%g" % lam]["error_vs_dense"] = dict(
+                o_max_abs=float(diff.abs().max().item()), row_rel_l2_max=float(rel.max().item()),
+                row_rel_l2_mean=float(rel.mean().item()), lse_max_abs=float((lse - lse0).abs().max().item()),
+                rows_changed=round(float((rel > 0).float().mean().item()), 5))
+            del diff, rel
+    del o0, lse0
     dense = out["0"]["ms"]
     for k, v in out.items():
         v["speedup_vs_lambda0"] = round(dense / v["ms"], 4)
