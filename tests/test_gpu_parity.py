@@ -84,6 +84,9 @@ PREFILL_SMALL = [
     # 16 (sequence, head group) pairs over 21 query blocks: on a 256-CU device 16 blocks are resident
     # at once, so the kv-group -> XCD map turns once
     (2, 16, 4, 2600, 128, 128, 0.02),
+    # odd G (one head per workgroup): 24 head groups over 12 query blocks, 10 resident at once on a
+    # 256-CU device, so the map turns there too
+    (1, 24, 8, 1500, 128, 128, 0.02),
 ]
 
 
