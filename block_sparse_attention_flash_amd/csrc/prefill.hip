@@ -411,6 +411,35 @@ __global__ __launch_bounds__(2 * BC * HPW) void prefill_kernel(PrefillArgs a) {
         if (issued) asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(CPW) : "memory");
         else asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     };
+    // Two head groups: the phase's whole tile copy is issued by the group in phase X, CPX
+    // pieces per wave, and the group in phase Y issues none.  Issuing a share of every copy
+    // at its head cost the phase-Y wave -- the longer of each SIMD's two -- 7-14% of its
+    // phase, while the phase-X wave waited 17-24% of its phase at the closing barrier.  A
+    // copy issued in phase p is waited for when its waves close phase p + 1 (in phase Y
+    // then, with nothing of their own in flight).
+    constexpr int CPX = 2 * CPW;
+    auto open_phase_x = [&](int p) -> bool {
+        const int jn = (p & 1) ? (p + 1) / 2 : p / 2 + 1;
+        if (jn >= jend) return false;
+        const uint16_t* tbase = ((p & 1) ? vbase : kbase) + (size_t)jn * BC * D;
+        char* tile = (p & 1) ? &lds_v[jn & 1][0] : &lds_k[jn & 1][0];
+        if (__builtin_expect(tile_is_ragged<BC>(jn, T), 0)) {
+#pragma unroll
+            for (int f = 0; f < CPX; ++f)
+                global_to_lds16_sbase(tbase, tile_copy_clamp<CPR, BC>(tile_copy_offset<CPR>(wrow, CPX, f, lane), jn, T),
+                                      lds_addr(tile + (wrow * CPX + f) * 1024));
+        } else {
+#pragma unroll
+            for (int f = 0; f < CPX; ++f)
+                global_to_lds16_sbase(tbase, tile_copy_offset<CPR>(wrow, CPX, f, lane),
+                                      lds_addr(tile + (wrow * CPX + f) * 1024));
+        }
+        return true;
+    };
+    auto close_phase_x = [&](bool issued) {
+        if (issued) asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(CPX) : "memory");
+        else asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    };
     // The wave in phase Y gets the higher issue priority: its PV MFMAs then take
     // the matrix unit as soon as they are ready (between the S MFMAs of the wave
     // in phase X) instead of stalling its in-order VALU stream behind them.
@@ -420,29 +449,36 @@ __global__ __launch_bounds__(2 * BC * HPW) void prefill_kernel(PrefillArgs a) {
     issue_v(0, 0);
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CPW) : "memory");  // K(0)
     __syncthreads();
-    if (HPW == 1 || hsub == 0) {
+    if (HPW == 1) {
         for (int j = 0; j < jend; ++j) {
             bool is = open_phase(2 * j);
             phase_x(j);
             close_phase(is);
             is = open_phase(2 * j + 1);
-            raise_prio();
             phase_y(j);
-            lower_prio();
             close_phase(is);
         }
-        if (HPW == 2) close_phase(open_phase(2 * jend));
-    } else {
-        close_phase(open_phase(0));
+    } else if (hsub == 0) {
         for (int j = 0; j < jend; ++j) {
-            bool is = open_phase(2 * j + 1);
+            const bool is = open_phase_x(2 * j);
             phase_x(j);
-            close_phase(is);
-            is = open_phase(2 * j + 2);
+            close_phase_x(is);
             raise_prio();
             phase_y(j);
             lower_prio();
-            close_phase(is);
+            close_phase_x(false);
+        }
+        close_phase_x(false);  // phase 2 jend: the other group's last phase Y; no copy
+    } else {
+        close_phase_x(false);  // phase 0: the other group's X(0), which issues its copy
+        for (int j = 0; j < jend; ++j) {
+            const bool is = open_phase_x(2 * j + 1);
+            phase_x(j);
+            close_phase_x(is);
+            raise_prio();
+            phase_y(j);
+            lower_prio();
+            close_phase_x(false);
         }
     }
 

@@ -77,7 +77,9 @@ void check_config(int NW, const std::vector<int>& lengths) {
 int main() {
     std::vector<int> lengths = {1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 300, 513, 1000, 1024, 4097,
                                 9000, 32768, 32769};
-    for (int hpw = 1; hpw <= 2; ++hpw) {  // waves per workgroup: Bc/32 per head, one or two heads
+    // issuing waves: Bc/32 (one head per workgroup; or, with two heads, the group in phase X,
+    // which issues each phase's whole tile), or 2 Bc/32 (both heads' waves: the first K and V tiles)
+    for (int hpw = 1; hpw <= 2; ++hpw) {
         check_config<64, 64>(2 * hpw, lengths);
         check_config<64, 128>(4 * hpw, lengths);
         check_config<128, 64>(2 * hpw, lengths);
