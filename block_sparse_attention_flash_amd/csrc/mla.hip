@@ -369,35 +369,47 @@ __global__ __launch_bounds__(512) void mla_pipe_kernel(MlaArgs a) {
     const int h0 = hgrp * HG;
     const uint16_t* kvb = a.kv + (size_t)b * N * MLA_DQK;
 
-    // every wave copies latent rows wave, wave + 8, wave + 16, wave + 24 of a
-    // sub-block (one 1 KiB instruction each, lane l at physical chunk l), and
-    // waves 0-3 one rotary copy of 8 rows each (lane l -> row 8w + l/8, chunk l % 8)
-    const bool rope_wave = wave < SB / 8;
+    // The sub-block copies are issued by one role's four waves: latent rows iw + 4 i (i < 8;
+    // one 1 KiB instruction each, lane l at physical chunk l) and one rotary copy of 8 rows
+    // (lane l -> row 8 iw + l / 8, chunk l % 8), iw being the wave's index in its role.  A
+    // wave that issues a copy waits for the CU's address unit to take it, and every wave
+    // issuing its share right after the step's barrier held all of them back: the role with
+    // slack issues them all -- the S waves with 64-token blocks (107.9 -> 105.6 us on
+    // decode_mla_32k), the P V waves with 32-token blocks (107.1 -> 101.3 us); the other
+    // choice was 10-13% slower than all waves issuing.
+    constexpr bool S_ISSUES = BCM == 64;
+    constexpr int NIW = 4;                       // issuing waves
+    const int iw = S_ISSUES ? wave : wave - 4;
+    const bool issuer = S_ISSUES ? wave < 4 : wave >= 4;
+    const bool rope_wave = issuer;               // SB / 8 = 4 rotary copies: one per issuing wave
+    static_assert(SB / 8 == NIW, "one rotary copy per issuing wave");
+    constexpr int NPC = SB / NIW;                // latent copies per issuing wave per sub-block
     auto issue = [&](int t) {
+        if (!issuer) return;
         char* base = &lds_kv[t % NSTAGE][0];
 #pragma unroll
-        for (int i = 0; i < SB / W; ++i) {
-            const int r = wave + W * i;
+        for (int i = 0; i < NPC; ++i) {
+            const int r = iw + NIW * i;
             const int key = min(key_base + t * SB + r, N - 1);
             global_to_lds16(kvb + (size_t)key * MLA_DQK + 8 * nope_chunk(lane, r), lds_addr(base + r * NOPE_ROW));
         }
         if (rope_wave) {
-            const int r = 8 * wave + (lane >> 3);
+            const int r = 8 * iw + (lane >> 3);
             const int key = min(key_base + t * SB + r, N - 1);
             const int c = (lane & 7) ^ (r & 7);
-            global_to_lds16(kvb + (size_t)key * MLA_DQK + MLA_DN + 8 * c, lds_addr(base + NOPE_TILE + 8 * wave * ROPE_ROW));
+            global_to_lds16(kvb + (size_t)key * MLA_DQK + MLA_DN + 8 * c, lds_addr(base + NOPE_TILE + 8 * iw * ROPE_ROW));
         }
     };
     // sub-block t's copies are complete once only those of the nb sub-blocks issued after it are outstanding
     auto wait_after = [&](int nb) {
-        if (nb <= 0) {
+        if (nb <= 0 || !issuer) {
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         } else if (nb == 1) {
-            if (rope_wave) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(SB / W + 1) : "memory");
-            else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(SB / W) : "memory");
+            if (rope_wave) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NPC + 1) : "memory");
+            else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NPC) : "memory");
         } else {
-            if (rope_wave) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (SB / W + 1)) : "memory");
-            else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (SB / W)) : "memory");
+            if (rope_wave) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (NPC + 1)) : "memory");
+            else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NPC) : "memory");
         }
     };
 
