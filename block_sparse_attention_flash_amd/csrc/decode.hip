@@ -217,7 +217,8 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
         // two staging slots -- the same slots and copy pattern as the V pass --
         // and are read back in the MFMA A layout (ds_read_b128).  Units past
         // the split re-read its last block (cached), so the wait counts are fixed.
-        // Unit u of the wave uses slot u % NSLOT.
+        // K keeps the default cache policy: both workgroups of a pair read these
+        // rows, the second from L2.  Unit u of the wave uses slot u % NSLOT.
         auto slot_of = [&](int u) { return lds_v + (NSLOT * wave + (u % NSLOT)) * VSLOT; };
         auto issue_k = [&](int u) {
             const int U = wave + W * u;
@@ -295,14 +296,14 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
             }
         };
         auto vslot_of = [&](int u) { return lds_v + NSLOT * wave * VSLOT + (u % VD) * (VSLOT / DSPLIT); };
-        auto issue_v = [&](int u) {
+        auto issue_v = [&](int u) {  // V rows are read once per pass: non-temporal copies
             const char* slot = vslot_of(u);
 #pragma unroll
             for (int f = 0; f < FRV; ++f) {
                 const int p = 64 * f + lane;
                 const int row = p / CPRV, cc = (p % CPRV) ^ (row & (CPRV - 1));
                 const int key = min(ukey0[u] + row, N - 1);
-                global_to_lds16(vbase + (size_t)key * D + half * DV + cc * 8, lds_addr(slot + 1024 * f));
+                global_to_lds16<true>(vbase + (size_t)key * D + half * DV + cc * 8, lds_addr(slot + 1024 * f));
             }
         };
         // this wave's kept units among the first VD (known after the early decisions)
@@ -808,7 +809,7 @@ __global__ __launch_bounds__(512) void decode_wide_kernel(DecodeArgs a) {
             if (!cpv) return;
             const uint16_t* tbase = vbase + (size_t)jj * BC * D;
             const uint32_t off = tile_is_ragged<BC>(jj, N) ? tile_copy_clamp<CPR, BC>(toff[f], jj, N) : toff[f];
-            global_to_lds16_sbase(tbase, off, lds_addr(lds_v[x] + (wave * CPW + f) * 1024));
+            global_to_lds16_sbase<true>(tbase, off, lds_addr(lds_v[x] + (wave * CPW + f) * 1024));
         };
         if (!vkeep_prev) {
 #pragma unroll
@@ -979,7 +980,7 @@ __global__ __launch_bounds__(64 * W) void decode_dense_kernel(DecodeArgs a) {
             const int p = 64 * f + lane;
             const int row = p / CPRV, cc = (p % CPRV) ^ (row & (CPRV - 1));
             const int key = min(key0 + row, N - 1);
-            global_to_lds16(vbase + (size_t)key * D + cc * 8, lds_addr(slot + KSLOT + 1024 * f));
+            global_to_lds16<true>(vbase + (size_t)key * D + cc * 8, lds_addr(slot + KSLOT + 1024 * f));
         }
     };
     for (int u = 0; u < min(NSLOT, nu); ++u) issue(u);
@@ -1160,7 +1161,7 @@ __global__ __launch_bounds__(512) void decode_load_only_kernel(DecodeArgs a) {
         for (int f = 0; f < FRV; ++f) {
             const int p = 64 * f + lane, row = p / CPRV, cc = (p % CPRV) ^ (row & (CPRV - 1));
             const int key = min(key_base + 32 * U + row, N - 1);
-            global_to_lds16(vbase + (size_t)key * D + cc * 8, lds_addr(slot + 1024 * f));
+            global_to_lds16<true>(vbase + (size_t)key * D + cc * 8, lds_addr(slot + 1024 * f));
         }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");

@@ -25,7 +25,8 @@ VALU_SGPR_WAIT, SALU_M0_WAIT = 5, 1
 
 
 def sgprs(tok):
-    tok = tok.strip().rstrip(",")
+    # an operand, possibly followed by cache-policy modifiers ("s[4:5] nt")
+    tok = (tok.split() or [""])[0].rstrip(",")
     if tok == "m0":
         return {"m0"}
     m = re.match(r"s\[(\d+):(\d+)\]$", tok)
@@ -88,3 +89,16 @@ def test_copies_have_their_wait_states(src, tmp_path):
     assert copies > 0
     bad = violations(asm)
     assert not bad, "%d of %d copies lack wait states, e.g.:\n%s" % (len(bad), copies, "\n".join(bad[:10]))
+
+
+def _kernel(body):
+    return "_Zcopy_kernel:\n" + "".join("\t%s\n" % ln for ln in body) + ".Lfunc_end0:\n"
+
+
+@pytest.mark.parametrize("policy", ["", " nt"])
+def test_checker_sees_the_base_pair_with_any_cache_policy(policy):
+    copy = "global_load_lds_dwordx4 v1, s[4:5]" + policy
+    early = _kernel(["s_mov_b32 m0, s9", "s_nop 0", "v_readfirstlane_b32 s5, v2", "s_nop 2", copy])
+    assert violations(early) and "s5" in violations(early)[0]
+    assert not violations(_kernel(["v_readfirstlane_b32 s5, v2", "s_mov_b32 m0, s9", "s_nop 4", copy]))
+    assert violations(_kernel(["s_mov_b32 m0, s9", copy]))  # M0 written right before the copy
