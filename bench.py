@@ -4,8 +4,9 @@
 One step = one split-KV decode step at 32K context (Llama-3.1-8B-like layer:
 B=1, Hq=32, Hkv=8, d=128, N=32768, Bc=128, lambda=1e-3, 16 splits) followed by
 the log-sum-exp combine, on seeded synthetic heavy-tailed inputs.  The KV cache
-is rotated over several identical copies so the working set exceeds twice the
-256 MB Infinity Cache and every step reads from HBM.
+is rotated over identical copies, about 2 GiB in all (eight times the 256 MB
+Infinity Cache), so every step reads from HBM whatever cache policy the
+kernels' loads carry.
 
 Printed: one JSON line whose `value` is the decode step's algorithmic HBM
 throughput (GB/s: all of K, the kept V blocks, q, the split partials and the
@@ -76,7 +77,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--copies", type=int, default=4, help="KV copies rotated to defeat the Infinity Cache")
+    p.add_argument("--copies", type=int, default=None,
+                   help="KV copies rotated to defeat the Infinity Cache (default: enough for 2 GiB)")
     p.add_argument("--prefill-reps", type=int, default=5, help="launches per prefill timing trial")
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-mla", action="store_true")
@@ -107,6 +109,37 @@ def parse():
 
 
 COPY_BYTES = 512 << 20  # plain device-to-device copy used to calibrate byte counters
+ROTATE_BYTES = 2 << 30  # KV bytes a timed loop rotates through: 8x the 256 MB Infinity Cache
+
+
+def kv_copies(args, footprint):
+    """Copies of a KV cache of `footprint` bytes to rotate: --copies if given, else enough for ROTATE_BYTES.
+    Fewer would let the Infinity Cache serve part of each pass, and how much depends on the loads'
+    cache policy (non-temporal lines are not kept), so an A/B of policies would time the cache."""
+    if args.copies:
+        return max(1, args.copies)
+    return max(1, int(np.ceil(ROTATE_BYTES / footprint)))
+
+
+def interleaved_trials(torch, stream, fns, reps, warm=1):
+    """(median, min, max) time in ms of each of fns over TRIALS rounds; every round runs each fn reps
+    times in turn, so clock and thermal drift during a run weigh on every point alike (timed one after
+    another, the first points ran up to 6% slower while the clocks ramped)."""
+    for fn in fns:
+        for _ in range(warm):
+            fn()
+    torch.cuda.synchronize()
+    ts = [[] for _ in fns]
+    for _ in range(TRIALS):
+        for i, fn in enumerate(fns):
+            s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s0.record(stream)
+            for _ in range(reps):
+                fn()
+            s1.record(stream)
+            torch.cuda.synchronize()
+            ts[i].append(s0.elapsed_time(s1) / reps)
+    return [(float(np.median(t)), min(t), max(t)) for t in ts]
 TRIALS = 7  # repeated kernel-only timing trials (median reported)
 
 
@@ -123,7 +156,9 @@ def profile_target(args, lib, torch, W):
         return
     if args.profile_target in ("decode_dense", "decode_ceiling"):
         w = W.CONFIGS["decode_32k"]
-        copies = [{k: dev(v) for k, v in W.generate(w).items()} for _ in range(max(1, args.copies))]
+        c0 = {k: dev(v) for k, v in W.generate(w).items()}
+        copies = [c0] + [{k: v.clone() for k, v in c0.items()}
+                         for _ in range(kv_copies(args, 2 * c0["k"].nbytes) - 1)]
         B, Hq, N, d, Bc, S = w.B, w.Hq, w.T, w.d, w.Bc, w.num_splits
         o_part = torch.empty((B, Hq, S, d), dtype=torch.float32, device="cuda")
         lse_part = torch.empty((B, Hq, S), dtype=torch.float32, device="cuda")
@@ -149,8 +184,9 @@ def profile_target(args, lib, torch, W):
             w = W.CONFIGS["decode_32k" if args.profile_target == "decode" else "decode_mqa_16k"]
             if args.profile_lambda is not None:
                 w = w.with_(lambdas=(args.profile_lambda,))
-        ncopies = 1 if args.profile_target == "decode_sweep128" else max(1, args.copies)
-        copies = [{k: dev(v) for k, v in W.generate(w).items()} for _ in range(ncopies)]
+        c0 = {k: dev(v) for k, v in W.generate(w).items()}
+        ncopies = 1 if args.profile_target == "decode_sweep128" else kv_copies(args, 2 * c0["k"].nbytes)
+        copies = [c0] + [{k: v.clone() for k, v in c0.items()} for _ in range(ncopies - 1)]
         B, Hq, N, d, Bc, S = w.B, w.Hq, w.T, w.d, w.Bc, w.num_splits
         nk = -(-N // Bc)
         o_part = torch.empty((B, Hq, S, d), dtype=torch.float32, device="cuda")
@@ -272,7 +308,7 @@ def bench_decode(args, lib, torch, W):
     w = W.CONFIGS["decode_32k"]
     lam = w.lambdas[0]
     x = W.generate(w)
-    copies = [{k: dev(v) for k, v in x.items()} for _ in range(max(1, args.copies))]
+    copies = [{k: dev(v) for k, v in x.items()} for _ in range(kv_copies(args, 2 * x["k"].nbytes))]
     B, Hq, N, d, Bc, S = w.B, w.Hq, w.T, w.d, w.Bc, w.num_splits
     nk = -(-N // Bc)
     f32 = dict(dtype=torch.float32, device="cuda")
@@ -402,7 +438,7 @@ def bench_decode(args, lib, torch, W):
         r["speedup_vs_lambda0"] = round(l0 / r["split_kernel_us"], 4)
     return dict(w=w, x=x, step_ms=step_ms, split_ms=split_ms, split_trials_ms=trials, lambda0_step_ms=lambda0_step_ms,
                 dense_step_ms=dense_step_ms, dense_kernel_ms=dense_kernel_ms, load_ceiling_ms=load_ceiling_ms,
-                wall=wall, bytes=by,
+                wall=wall, bytes=by, kv_copies_rotated=len(copies),
                 block_sparsity=float(sk.mean()), vload_sparsity=float(vsk.mean()), lambda_sweep=sweep)
 
 
@@ -525,7 +561,7 @@ def bench_config(name, args, lib, torch, W):
                     block_sparsity=round(skipped / visited, 5))
     S = w.num_splits
     footprint = 2 * x["k"].nbytes
-    ncopy = max(1, min(args.copies, int(np.ceil(600e6 / footprint))))
+    ncopy = kv_copies(args, footprint)
     xs = [{k: dev(v) for k, v in x.items()} for _ in range(ncopy)]
     del x
     o_part = torch.empty((B, Hq, S, d), **f32)
@@ -695,23 +731,7 @@ def bench_decode_length_sweep(args, lib, torch, W, bsa):
         if st != 0:
             raise RuntimeError("libblasst call failed with status %d" % st)
 
-    def trials(fn, reps=20):
-        for _ in range(3):
-            fn()
-        torch.cuda.synchronize()
-        ts = []
-        for _ in range(TRIALS):
-            s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            s0.record(stream)
-            for _ in range(reps):
-                fn()
-            s1.record(stream)
-            torch.cuda.synchronize()
-            ts.append(s0.elapsed_time(s1) / reps)
-        return float(np.median(ts)), min(ts), max(ts)
-
-    dense_ms = trials(lambda: ok(lib.blasst_decode_dense(P(x["q"]), P(x["k"]), P(x["v"]), P(o_part), P(lse_part),
-                                                          B, Hq, N, d, w.G, Bc, S, sp)))
+    dense_a = (P(x["q"]), P(x["k"]), P(x["v"]), P(o_part), P(lse_part), B, Hq, N, d, w.G, Bc, S, sp)
     targets = {"a/L, 50%": policy.lambda_for(0.5, L, alpha, beta), "a/L, 70%": policy.lambda_for(0.7, L, alpha, beta)}
     # sparsity-matched points: lambda read off these sequences' own margins (block sparsity 50%, and the
     # 73.2% at which the blog quotes its decode speed-up)
@@ -722,14 +742,18 @@ def bench_decode_length_sweep(args, lib, torch, W, bsa):
     points = [("lambda = 0", 0.0), ("fixed 1e-3", 1e-3), ("fixed 3e-3", 3e-3)] + list(targets.items()) + \
         list(matched.items())
     dense_bytes = decode_bytes(w, np.zeros((B, w.Hkv, nk), np.uint8))["split"]
-    rows = []
+    stats, fns = [], []
     for label, lam in points:
         a = (P(x["q"]), P(x["k"]), P(x["v"]), P(o_part), P(lse_part), P(skip), P(vskip), B, Hq, N, d, w.G, Bc,
              ctypes.c_double(lam), 1, S, sp)
-        ms = trials(lambda: ok(lib.blasst_decode(*a)))
         ok(lib.blasst_decode(*a))
         torch.cuda.synchronize()
-        sk, vsk = skip.cpu().numpy(), vskip.cpu().numpy()
+        stats.append((skip.cpu().numpy(), vskip.cpu().numpy()))
+        fns.append(lambda a=a: ok(lib.blasst_decode(*a)))
+    times = interleaved_trials(torch, stream, [lambda: ok(lib.blasst_decode_dense(*dense_a))] + fns, 20, warm=3)
+    dense_ms = times[0]
+    rows = []
+    for (label, lam), (sk, vsk), ms in zip(points, stats, times[1:]):
         by = decode_bytes(w, vsk)["split"]
         rows.append(dict(point=label, lam=lam, split_kernel_us=round(ms[0] * 1e3, 2),
                          split_kernel_us_min=round(ms[1] * 1e3, 2), split_kernel_us_max=round(ms[2] * 1e3, 2),
@@ -780,22 +804,7 @@ def bench_prefill_length_sweep(args, lib, torch, W, bsa):
         if st != 0:
             raise RuntimeError("libblasst call failed with status %d" % st)
 
-    def trials(fn, reps=2):
-        fn()
-        torch.cuda.synchronize()
-        ts = []
-        for _ in range(TRIALS):
-            s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            s0.record(stream)
-            for _ in range(reps):
-                fn()
-            s1.record(stream)
-            torch.cuda.synchronize()
-            ts.append(s0.elapsed_time(s1) / reps)
-        return float(np.median(ts)), min(ts), max(ts)
-
-    no_test_ms = trials(lambda: ok(lib.blasst_prefill_dense(P(x["q"]), P(x["k"]), P(x["v"]), P(o), P(lse),
-                                                            B, Hq, T, d, w.G, Bc, 1, sp)))
+    no_test_a = (P(x["q"]), P(x["k"]), P(x["v"]), P(o), P(lse), B, Hq, T, d, w.G, Bc, 1, sp)
     targets = {"a/L, 50%": policy.lambda_for(0.5, L, alpha, beta), "a/L, 70%": policy.lambda_for(0.7, L, alpha, beta)}
     # sparsity-matched points: lambda read off this sequence's own margins (block sparsity 50%, and the
     # 71.9% at which the blog quotes its prefill speed-up)
@@ -805,13 +814,18 @@ def bench_prefill_length_sweep(args, lib, torch, W, bsa):
     del own
     points = [("lambda = 0", 0.0), ("fixed 1e-3", 1e-3), ("fixed 3e-3", 3e-3)] + list(targets.items()) + \
         list(matched.items())
-    rows = []
+    skips, fns = [], []
     for label, lam in points:
         a = (P(x["q"]), P(x["k"]), P(x["v"]), P(o), P(lse), P(mask), B, Hq, T, d, w.G, Bc,
              ctypes.c_double(lam), 1, sp)
-        ms = trials(lambda: ok(lib.blasst_prefill(*a)))
+        ok(lib.blasst_prefill(*a))
         torch.cuda.synchronize()
-        skipped = int((mask == 1).sum().item())
+        skips.append(int((mask == 1).sum().item()))
+        fns.append(lambda a=a: ok(lib.blasst_prefill(*a)))
+    times = interleaved_trials(torch, stream, [lambda: ok(lib.blasst_prefill_dense(*no_test_a))] + fns, 2)
+    no_test_ms = times[0]
+    rows = []
+    for (label, lam), skipped, ms in zip(points, skips, times[1:]):
         kept = visited - skipped
         flops = (visited + kept) * tile_flops
         rows.append(dict(point=label, lam=lam, ms=round(ms[0], 3), ms_min=round(ms[1], 3), ms_max=round(ms[2], 3),
@@ -851,19 +865,8 @@ def speedup_curve(args, lib, torch, W, bsa):
         if st != 0:
             raise RuntimeError("libblasst call failed with status %d" % st)
 
-    def trials(fn, reps):
-        fn()
-        torch.cuda.synchronize()
-        ts = []
-        for _ in range(TRIALS):
-            s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            s0.record(stream)
-            for _ in range(reps):
-                fn()
-            s1.record(stream)
-            torch.cuda.synchronize()
-            ts.append(s0.elapsed_time(s1) / reps)
-        return float(np.median(ts))
+    def interleaved(fns, reps):
+        return [t[0] for t in interleaved_trials(torch, stream, fns, reps, warm=0)]
 
     out = {}
     # ---- decode, 128K
@@ -877,18 +880,22 @@ def speedup_curve(args, lib, torch, W, bsa):
     skip = torch.empty((B, Hq, nk), dtype=torch.uint8, device="cuda")
     vskip = torch.empty((B, w.Hkv, nk), dtype=torch.uint8, device="cuda")
     own, _ = bsa.decode_margins(x["q"], x["k"], S, Bc=Bc)
-    dense_us = 1e3 * trials(lambda: ok(lib.blasst_decode_dense(P(x["q"]), P(x["k"]), P(x["v"]), P(o_part),
-                                                               P(lse_part), B, Hq, N, d, w.G, Bc, S, sp)), 20)
-    rows = []
+    dense_a = (P(x["q"]), P(x["k"]), P(x["v"]), P(o_part), P(lse_part), B, Hq, N, d, w.G, Bc, S, sp)
+    rows, fns = [], []
     for target in CURVE_TARGETS:
         lam = policy.lambda_at_sparsity(own, target) if target > 0 else 0.0
         a = (P(x["q"]), P(x["k"]), P(x["v"]), P(o_part), P(lse_part), P(skip), P(vskip), B, Hq, N, d, w.G, Bc,
              ctypes.c_double(lam), 1, S, sp)
-        us = 1e3 * trials(lambda: ok(lib.blasst_decode(*a)), 20)
-        by = decode_bytes(w, vskip.cpu().numpy())["split"]
+        ok(lib.blasst_decode(*a))
+        torch.cuda.synchronize()
         rows.append(dict(target=target, lam=lam, block_sparsity=round(float(skip.float().mean().item()), 4),
-                         vload_sparsity=round(float(vskip.float().mean().item()), 4), us=round(us, 2),
-                         bytes_per_launch=by))
+                         vload_sparsity=round(float(vskip.float().mean().item()), 4),
+                         bytes_per_launch=decode_bytes(w, vskip.cpu().numpy())["split"]))
+        fns.append(lambda a=a: ok(lib.blasst_decode(*a)))
+    times = interleaved([lambda: ok(lib.blasst_decode_dense(*dense_a))] + fns, 20)
+    dense_us = 1e3 * times[0]
+    for r, t in zip(rows, times[1:]):
+        r["us"] = round(1e3 * t, 2)
     for r in rows:
         r["speedup_vs_lambda0"] = round(rows[0]["us"] / r["us"], 4)
         r["speedup_vs_dense_kernel"] = round(dense_us / r["us"], 4)
@@ -909,15 +916,19 @@ def speedup_curve(args, lib, torch, W, bsa):
         own = bsa.prefill_margins(x["q"], x["k"], Bc=Bc, causal=True)
         visited = B * Hq * nq * (nq + 1) // 2
         reps = max(1, (131072 // T) ** 2 // 4)
-        rows = []
+        rows, fns = [], []
         for target in CURVE_TARGETS:
             lam = policy.lambda_at_sparsity(own, target) if target > 0 else 0.0
             a = (P(x["q"]), P(x["k"]), P(x["v"]), P(o), P(lse), P(mask), B, Hq, T, d, w.G, Bc,
                  ctypes.c_double(lam), 1, sp)
-            ms = trials(lambda: ok(lib.blasst_prefill(*a)), reps)
+            ok(lib.blasst_prefill(*a))
+            torch.cuda.synchronize()
             kept = visited - int((mask == 1).sum().item())
-            rows.append(dict(target=target, lam=lam, block_sparsity=round(1 - kept / visited, 4), ms=round(ms, 3),
+            rows.append(dict(target=target, lam=lam, block_sparsity=round(1 - kept / visited, 4),
                              flops_bound=round(2 * visited / (visited + kept), 4)))
+            fns.append(lambda a=a: ok(lib.blasst_prefill(*a)))
+        for r, t in zip(rows, interleaved(fns, reps)):
+            r["ms"] = round(t, 3)
         for r in rows:
             r["speedup_vs_lambda0"] = round(rows[0]["ms"] / r["ms"], 4)
         out["prefill_%dk" % (L // 1024)] = dict(B=B, Hq=Hq, Hkv=w.Hkv, d=d, context=T, Bc=Bc, causal=True,
@@ -935,7 +946,7 @@ def bench_mla(args, lib, torch, W):
     x = W.generate(w, parts=("q", "k"))
     q = dev(np.ascontiguousarray(x["q"][:, :, 0]))
     kvs = [dev(np.ascontiguousarray(x["k"][:, 0]))]
-    kvs.append(kvs[0].clone())  # two copies, 604 MB: beyond the Infinity Cache
+    kvs += [kvs[0].clone() for _ in range(kv_copies(args, kvs[0].nbytes) - 1)]
     del x
     B, Hq, N, dqk, dv, S = w.B, w.Hq, w.T, w.d, w.dv, w.num_splits
     stream = torch.cuda.current_stream()
@@ -956,14 +967,14 @@ def bench_mla(args, lib, torch, W):
                       ctypes.c_double(w.score_scale), ctypes.c_double(lam), S, ctypes.c_void_p(stream.cuda_stream))
                      for kv in kvs]
             for i in range(20):  # warm-up (the first lambda's trials otherwise see the clocks ramp)
-                assert lib.blasst_decode_mla(*args_[i % 2]) == 0
+                assert lib.blasst_decode_mla(*args_[i % len(args_)]) == 0
             torch.cuda.synchronize()
             ts = []
             for _ in range(TRIALS):
                 s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 s0.record(stream)
                 for i in range(20):
-                    assert lib.blasst_decode_mla(*args_[i % 2]) == 0
+                    assert lib.blasst_decode_mla(*args_[i % len(args_)]) == 0
                 s1.record(stream)
                 torch.cuda.synchronize()
                 ts.append(s0.elapsed_time(s1) * 1e3 / 20)
@@ -984,7 +995,8 @@ def bench_mla(args, lib, torch, W):
             v["speedup_vs_lambda0"] = round(dense / v["us"], 4)
         by_block["Bc%d" % Bc] = dict(heads_per_workgroup=hg, pv_skip_unit_heads=tile, by_lambda=out)
     by = B * N * dqk * 2
-    return dict(workload=w.name, B=B, Hq=Hq, d_qk=dqk, d_v=dv, context=N, num_splits=S, by_block=by_block,
+    return dict(workload=w.name, B=B, Hq=Hq, d_qk=dqk, d_v=dv, context=N, num_splits=S, kv_copies_rotated=len(kvs),
+                by_block=by_block,
                 hbm_roofline_us=round(by / (HBM_PEAK_GBS * 1e3), 2),
                 mfma_roofline_us_dense=round(2.0 * (dqk + dv) * N * Hq * B / (MFMA_BF16_PEAK_TFLOPS * 1e6), 2))
 
@@ -1106,7 +1118,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "kind": "split-KV decode + LSE combine", "B": w.B, "Hq": w.Hq,
                    "Hkv": w.Hkv, "d": w.d, "context": w.T, "Bc": w.Bc, "lambda": w.lambdas[0],
-                   "num_splits": w.num_splits, "kv_copies_rotated": args.copies},
+                   "num_splits": w.num_splits, "kv_copies_rotated": d["kv_copies_rotated"]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic("decode_split_kernel", w.name),

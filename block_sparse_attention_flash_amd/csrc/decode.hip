@@ -41,6 +41,8 @@
 // and the test reads t~ - m < ln(lambda) * log2(e).
 #include "device_common.h"
 #include "kernels.h"
+
+#include <type_traits>
 #include <climits>
 #include <mutex>
 
@@ -73,7 +75,10 @@ __device__ __forceinline__ void wait_vm(int n) {
 // on one XCD, so the K and V blocks they share come from HBM once.  The V skip
 // mask is then an OR of the parts' "loaded" votes: the launcher sets it to
 // "not loaded" first and each part clears the bytes of the blocks it loads.
-template <int D, int BC, int NT, int UW, int W, int NSLOT, bool MARGINS = false, int DSPLIT = 1, int HS = 1>
+// ONEPHASE: every split spans at most one phase (the launcher checks), so K
+// is non-temporal throughout (see the K pass) with no per-unit branch.
+template <int D, int BC, int NT, int UW, int W, int NSLOT, bool MARGINS = false, int DSPLIT = 1, int HS = 1,
+          bool ONEPHASE = false>
 __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
     constexpr int KG = BC / 32;           // 32-key units per block
     constexpr int UPP = W * UW;           // units per phase
@@ -217,10 +222,16 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
         // two staging slots -- the same slots and copy pattern as the V pass --
         // and are read back in the MFMA A layout (ds_read_b128).  Units past
         // the split re-read its last block (cached), so the wait counts are fixed.
-        // K keeps the default cache policy: both workgroups of a pair read these
-        // rows, the second from L2.  Unit u of the wave uses slot u % NSLOT.
+        // Unit u of the wave uses slot u % NSLOT.  Cache policy: non-temporal
+        // where no other workgroup reads the rows, and in a split's first phase,
+        // where the two workgroups of a pair start together and the second one's
+        // reads still find the first one's lines in L2.  Later phases of a pair
+        // keep the default policy: the pair drifts apart, and non-temporal lines
+        // left L2 before the second read (a 32K-key split ran 1.36x slower).  Head
+        // parts (HS > 1) share K and V for the whole pass: default policy.
+        const bool k_stream = HS == 1 && (DSPLIT == 1 || ONEPHASE || p0 == j0);
         auto slot_of = [&](int u) { return lds_v + (NSLOT * wave + (u % NSLOT)) * VSLOT; };
-        auto issue_k = [&](int u) {
+        auto issue_k_as = [&](int u, auto stream) {
             const int U = wave + W * u;
             const int key0 = min(p0 + U / KG, j1 - 1) * BC + (U % KG) * 32;
             const char* slot = slot_of(u);
@@ -229,8 +240,12 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
                 const int p = 64 * f + lane;
                 const int row = p / CPR, cc = (p % CPR) ^ (row & (CPR - 1));
                 const int key = min(key0 + row, N - 1);
-                global_to_lds16(kbase + (size_t)key * D + cc * 8, lds_addr(slot + 1024 * f));
+                global_to_lds16<decltype(stream)::value>(kbase + (size_t)key * D + cc * 8, lds_addr(slot + 1024 * f));
             }
+        };
+        auto issue_k = [&](int u) {  // one uniform branch per unit, not per copy
+            if (k_stream) issue_k_as(u, std::true_type{});
+            else issue_k_as(u, std::false_type{});
         };
 #pragma unroll
         for (int u = 0; u < (NSLOT < UW ? NSLOT : UW); ++u) issue_k(u);
@@ -296,14 +311,14 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
             }
         };
         auto vslot_of = [&](int u) { return lds_v + NSLOT * wave * VSLOT + (u % VD) * (VSLOT / DSPLIT); };
-        auto issue_v = [&](int u) {  // V rows are read once per pass: non-temporal copies
+        auto issue_v = [&](int u) {
             const char* slot = vslot_of(u);
 #pragma unroll
             for (int f = 0; f < FRV; ++f) {
                 const int p = 64 * f + lane;
                 const int row = p / CPRV, cc = (p % CPRV) ^ (row & (CPRV - 1));
                 const int key = min(ukey0[u] + row, N - 1);
-                global_to_lds16<true>(vbase + (size_t)key * D + half * DV + cc * 8, lds_addr(slot + 1024 * f));
+                global_to_lds16<HS == 1>(vbase + (size_t)key * D + half * DV + cc * 8, lds_addr(slot + 1024 * f));
             }
         };
         // this wave's kept units among the first VD (known after the early decisions)
@@ -656,12 +671,12 @@ __global__ __launch_bounds__(512) void decode_wide_kernel(DecodeArgs a) {
         if (__builtin_expect(tile_is_ragged<BC>(j, N), 0)) {
 #pragma unroll
             for (int f = 0; f < CPW; ++f)
-                global_to_lds16_sbase(tbase, tile_copy_clamp<CPR, BC>(toff[f], j, N),
+                global_to_lds16_sbase<true>(tbase, tile_copy_clamp<CPR, BC>(toff[f], j, N),
                                       lds_addr(tile + (wave * CPW + f) * 1024));
         } else {
 #pragma unroll
             for (int f = 0; f < CPW; ++f)
-                global_to_lds16_sbase(tbase, toff[f], lds_addr(tile + (wave * CPW + f) * 1024));
+                global_to_lds16_sbase<true>(tbase, toff[f], lds_addr(tile + (wave * CPW + f) * 1024));
         }
     };
     if (j0 < j1) issue(kbase, lds_k[0], j0);
@@ -965,6 +980,9 @@ __global__ __launch_bounds__(64 * W) void decode_dense_kernel(DecodeArgs a) {
 
     // unit u of this wave: keys key_base + 32 (wave + W u) ..; slot pair u % NSLOT
     auto pair_of = [&](int u) { return lds_kv + (NSLOT * wave + u % NSLOT) * PAIR; };
+    // V non-temporal as in the split kernel; K on the default cache policy, with
+    // which this kernel ran 4% faster (the split kernel runs faster with K
+    // non-temporal too)
     auto issue = [&](int u) {
         const int key0 = key_base + 32 * (wave + W * u);
         const char* slot = pair_of(u);
@@ -1120,8 +1138,9 @@ __global__ __launch_bounds__(64 * W) void decode_dense_kernel(DecodeArgs a) {
 // per split at lambda = 0 -- every 32-key K unit of the split by both
 // workgroups of the pair, then each workgroup half of every V row -- through
 // the same rings (eight waves, two 8 KiB slots each), with no arithmetic and
-// no barrier.  Its time is the floor those bytes and that access pattern set
-// for the decode kernel on this part.
+// no barrier, and with the same cache policies (K non-temporal in the split's
+// first phase of 64 units, V non-temporal).  Its time is the floor those bytes
+// and that access pattern set for the decode kernel on this part.
 template <int D, int BC>
 __global__ __launch_bounds__(512) void decode_load_only_kernel(DecodeArgs a) {
     constexpr int W = 8, NSLOT = 2;
@@ -1149,7 +1168,8 @@ __global__ __launch_bounds__(512) void decode_load_only_kernel(DecodeArgs a) {
         for (int f = 0; f < FR; ++f) {
             const int p = 64 * f + lane, row = p / CPR, cc = (p % CPR) ^ (row & (CPR - 1));
             const int key = min(key_base + 32 * U + row, N - 1);
-            global_to_lds16(kbase + (size_t)key * D + cc * 8, lds_addr(slot + 1024 * f));
+            if (U < 64) global_to_lds16<true>(kbase + (size_t)key * D + cc * 8, lds_addr(slot + 1024 * f));
+            else global_to_lds16<false>(kbase + (size_t)key * D + cc * 8, lds_addr(slot + 1024 * f));
         }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -1275,7 +1295,12 @@ template <int D, int BC, int NT, int UW, int W, int NSLOT>
 hipError_t launch_split_pairs(const DecodeArgs& a, hipStream_t stream) {
     const int64_t units = (int64_t)a.S * a.Hkv * a.B;
     const dim3 grid((unsigned)(2 * ((units + 7) / 8) * 8));
-    hipLaunchKernelGGL((decode_split_kernel<D, BC, NT, UW, W, NSLOT, false, 2>), grid, dim3(64 * W), 0, stream, a);
+    constexpr int BPP = W * UW / (BC / 32);  // blocks per phase
+    if ((a.nk + a.S - 1) / a.S <= BPP)       // every split (of any ragged length too) in one phase
+        hipLaunchKernelGGL((decode_split_kernel<D, BC, NT, UW, W, NSLOT, false, 2, 1, true>), grid, dim3(64 * W), 0,
+                           stream, a);
+    else
+        hipLaunchKernelGGL((decode_split_kernel<D, BC, NT, UW, W, NSLOT, false, 2>), grid, dim3(64 * W), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -90,12 +90,11 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // wait states this family needs before it are in the asm itself: one after a
 // scalar write of M0 (which the compiler emits right before the asm).
 // STREAM sets the non-temporal cache policy (nt), for rows that one pass reads
-// once and no other workgroup reads again: the decode kernels' V rows.  A 134 MB
-// decode pass runs 10-13% faster with it.  Rows that another workgroup reads
-// again from L2 keep the default policy: K in decode (both workgroups of a pair
-// read it; with K non-temporal as well the pass was 5% slower) and the prefill
-// tiles (shared by the query blocks of a kv head; non-temporal, prefill was 3%
-// slower).
+// once: the decode kernels' K and V.  A 134 MB decode pass runs 8% faster with
+// it (a plain streaming read of that size runs 5.6-5.9 TB/s with ordinary loads
+// and 6.1-6.5 TB/s with non-temporal ones).  The prefill tiles, which the query
+// blocks of a kv head share in L2, keep the default policy (non-temporal,
+// prefill ran 3% slower).
 template <bool STREAM = false>
 __device__ __forceinline__ void global_to_lds16(const void* gptr, uint32_t lds_base) {
     if constexpr (STREAM)
