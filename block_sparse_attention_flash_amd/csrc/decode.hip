@@ -157,6 +157,43 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
         }
     }
 
+    // Each unit's 32 K rows go HBM -> LDS (global_load_lds_dwordx4, whole rows per
+    // instruction, XOR-swizzled by 16-byte chunk) into the wave's staging slots;
+    // unit u of the wave (in the phase starting at block p0) uses slot u % NSLOT.
+    // Units past the split re-read its last block (cached), so the wait counts are
+    // fixed.  Cache policy: non-temporal where no other workgroup reads the rows,
+    // and in a split's first phase, where the two workgroups of a pair start
+    // together and the second one's reads still find the first one's lines in L2.
+    // Later phases of a pair keep the default policy: the pair drifts apart, and
+    // non-temporal lines left L2 before the second read (a 32K-key split ran 1.36x
+    // slower).  Head parts (HS > 1) share K and V for the whole pass: default policy.
+    auto slot_of = [&](int u) { return lds_v + (NSLOT * wave + (u % NSLOT)) * VSLOT; };
+    auto issue_k_as = [&](int p0, int u, auto stream) {
+        const int U = wave + W * u;
+        const int key0 = min(p0 + U / KG, j1 - 1) * BC + (U % KG) * 32;
+        const char* slot = slot_of(u);
+#pragma unroll
+        for (int f = 0; f < FR; ++f) {
+            const int p = 64 * f + lane;
+            const int row = p / CPR, cc = (p % CPR) ^ (row & (CPR - 1));
+            const int key = min(key0 + row, N - 1);
+            global_to_lds16<decltype(stream)::value>(kbase + (size_t)key * D + cc * 8, lds_addr(slot + 1024 * f));
+        }
+    };
+    // The first phase's first units go out before q is read: the compiler waits for
+    // the q loads before the phase loop, which would otherwise hold these copies back
+    // by a whole memory round trip (decode_32k: 24.14 -> 23.75 us).  The 8-wave launch
+    // with one workgroup per split keeps the old order: at d = 128, Bc = 64 the early
+    // copies would need one register more than its 256.
+    constexpr bool EARLY_K = !(DSPLIT == 1 && W == 8);
+    if (EARLY_K && j0 < j1) {
+#pragma unroll
+        for (int u = 0; u < (NSLOT < UW ? NSLOT : UW); ++u) {
+            if constexpr (HS == 1) issue_k_as(j0, u, std::true_type{});
+            else issue_k_as(j0, u, std::false_type{});
+        }
+    }
+
     // q^T as the B operand: lane (g, n) holds q[head n][32s + 8g .. +8].
     bf16x8 qf[QL ? 1 : NT][DS];
     bool head_ok[NT];
@@ -217,38 +254,19 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
         }
 
         // ================= K pass =================
-        // Each unit's 32 K rows go HBM -> LDS (global_load_lds_dwordx4, whole
-        // rows per instruction, XOR-swizzled by 16-byte chunk) into this wave's
-        // two staging slots -- the same slots and copy pattern as the V pass --
-        // and are read back in the MFMA A layout (ds_read_b128).  Units past
-        // the split re-read its last block (cached), so the wait counts are fixed.
-        // Unit u of the wave uses slot u % NSLOT.  Cache policy: non-temporal
-        // where no other workgroup reads the rows, and in a split's first phase,
-        // where the two workgroups of a pair start together and the second one's
-        // reads still find the first one's lines in L2.  Later phases of a pair
-        // keep the default policy: the pair drifts apart, and non-temporal lines
-        // left L2 before the second read (a 32K-key split ran 1.36x slower).  Head
-        // parts (HS > 1) share K and V for the whole pass: default policy.
+        // K units (issue_k_as above) in the wave's staging slots -- the same slots
+        // and copy pattern as the V pass -- read back in the MFMA A layout
+        // (ds_read_b128).  With EARLY_K the first phase's first units are already
+        // in flight.
         const bool k_stream = HS == 1 && (DSPLIT == 1 || ONEPHASE || p0 == j0);
-        auto slot_of = [&](int u) { return lds_v + (NSLOT * wave + (u % NSLOT)) * VSLOT; };
-        auto issue_k_as = [&](int u, auto stream) {
-            const int U = wave + W * u;
-            const int key0 = min(p0 + U / KG, j1 - 1) * BC + (U % KG) * 32;
-            const char* slot = slot_of(u);
-#pragma unroll
-            for (int f = 0; f < FR; ++f) {
-                const int p = 64 * f + lane;
-                const int row = p / CPR, cc = (p % CPR) ^ (row & (CPR - 1));
-                const int key = min(key0 + row, N - 1);
-                global_to_lds16<decltype(stream)::value>(kbase + (size_t)key * D + cc * 8, lds_addr(slot + 1024 * f));
-            }
-        };
         auto issue_k = [&](int u) {  // one uniform branch per unit, not per copy
-            if (k_stream) issue_k_as(u, std::true_type{});
-            else issue_k_as(u, std::false_type{});
+            if (k_stream) issue_k_as(p0, u, std::true_type{});
+            else issue_k_as(p0, u, std::false_type{});
         };
+        if (!EARLY_K || p0 != j0) {
 #pragma unroll
-        for (int u = 0; u < (NSLOT < UW ? NSLOT : UW); ++u) issue_k(u);
+            for (int u = 0; u < (NSLOT < UW ? NSLOT : UW); ++u) issue_k(u);
+        }
         if constexpr (QL) {
             if (!q_staged) {  // first phase: q goes to LDS while the first K copies are in flight
 #pragma unroll
