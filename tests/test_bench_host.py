@@ -43,3 +43,19 @@ def test_counter_records_match_the_sources():
     # the bench line quotes these; a kernel change without re-taken counters turns them to null
     assert bench.measured_traffic("decode_split_kernel", "decode_32k") is not None
     assert bench.measured_traffic("prefill_kernel", "prefill_32k") is not None
+
+
+def test_rotation_defeats_the_infinity_cache():
+    # every timed loop rotates at least 2 GiB of KV (8x the 256 MB Infinity Cache), whatever the
+    # loads' cache policy keeps there; --copies overrides the count
+    class Args:
+        copies = None
+    for name in ("decode_32k", "decode_128k_b16", "decode_mqa_16k"):
+        w = W.CONFIGS[name]
+        footprint = 2 * w.B * w.Hkv * w.T * w.d * 2
+        n = bench.kv_copies(Args, footprint)
+        assert n * footprint >= bench.ROTATE_BYTES and (n - 1) * footprint < bench.ROTATE_BYTES
+    assert bench.kv_copies(Args, 2 * 1024 ** 3) == 1
+    assert bench.kv_copies(Args, 134217728) == 16
+    Args.copies = 3
+    assert bench.kv_copies(Args, 134217728) == 3
