@@ -953,47 +953,49 @@ def bench_mla(args, lib, torch, W):
     P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
     o_part = torch.empty((B, Hq, S, dv), dtype=torch.float32, device="cuda")
     lse_part = torch.empty((B, Hq, S), dtype=torch.float32, device="cuda")
-    by_block = {}
+    hg = 64 if Hq % 64 == 0 else 32
+    # the unit whose P V product a block skips only when every head in it skips: a 16-head
+    # tile in the 64-head pipeline, the whole 32-head workgroup in the 32-head kernel
+    tile = 16 if hg == 64 else 32
+    # every (block size, lambda) case is run once for its decisions, then all are timed
+    # interleaved (20 launches per case and round, the cache copies rotated)
+    cases, fns = [], []
     for Bc in (w.Bc, 32):
         nk = -(-N // Bc)
         skip = torch.empty((B, Hq, nk), dtype=torch.uint8, device="cuda")
-        hg = 64 if Hq % 64 == 0 else 32
-        # the unit whose P V product a block skips only when every head in it skips: a 16-head
-        # tile in the 64-head pipeline, the whole 32-head workgroup in the 32-head kernel
-        tile = 16 if hg == 64 else 32
-        out = {}
         for lam in (0.0,) + tuple(w.lambdas):
             args_ = [(P(q), P(kv), P(o_part), P(lse_part), P(skip), B, Hq, N, dqk, dv, Bc,
                       ctypes.c_double(w.score_scale), ctypes.c_double(lam), S, ctypes.c_void_p(stream.cuda_stream))
                      for kv in kvs]
-            for i in range(20):  # warm-up (the first lambda's trials otherwise see the clocks ramp)
-                assert lib.blasst_decode_mla(*args_[i % len(args_)]) == 0
+            assert lib.blasst_decode_mla(*args_[0]) == 0
             torch.cuda.synchronize()
-            ts = []
-            for _ in range(TRIALS):
-                s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                s0.record(stream)
+            cases.append((Bc, lam, skip.cpu().numpy().astype(bool)))
+
+            def fn(args_=args_):
                 for i in range(20):
                     assert lib.blasst_decode_mla(*args_[i % len(args_)]) == 0
-                s1.record(stream)
-                torch.cuda.synchronize()
-                ts.append(s0.elapsed_time(s1) * 1e3 / 20)
-            us = float(np.median(ts))
-            sk = skip.cpu().numpy().astype(bool)                          # [B, Hq, nk]
-            tile_kept = ~sk.reshape(B, Hq // tile, tile, nk).all(axis=2)  # P V formed for the tile
-            rows = np.minimum(Bc, N - Bc * np.arange(nk))                  # tokens per block
-            s_flops = 2.0 * dqk * N * Hq * B
-            pv_flops = 2.0 * dv * tile * float((tile_kept * rows).sum())
-            by = B * N * dqk * 2 + B * Hq * dqk * 2 + B * Hq * S * (dv + 1) * 4 + B * Hq * nk
-            out["%g" % lam] = dict(us=round(us, 2), us_min=round(min(ts), 2), us_max=round(max(ts), 2),
-                                   GBs=round(by / us / 1e3, 1), frac_of_hbm_peak=round(by / us / 1e3 / HBM_PEAK_GBS, 4),
-                                   tflops_executed=round((s_flops + pv_flops) / us / 1e6, 1),
-                                   block_sparsity=round(float(sk.mean()), 5),
-                                   pv_skipped_fraction=round(1.0 - float(tile_kept.mean()), 5))
-        dense = out["0"]["us"]
-        for v in out.values():
+            fns.append(fn)
+    times = interleaved_trials(torch, stream, fns, 1)
+    by_block = {}
+    for (Bc, lam, sk), (med, lo, hi) in zip(cases, times):
+        nk = -(-N // Bc)
+        us, us_lo, us_hi = med * 1e3 / 20, lo * 1e3 / 20, hi * 1e3 / 20
+        tile_kept = ~sk.reshape(B, Hq // tile, tile, nk).all(axis=2)  # P V formed for the tile
+        rows = np.minimum(Bc, N - Bc * np.arange(nk))                  # tokens per block
+        s_flops = 2.0 * dqk * N * Hq * B
+        pv_flops = 2.0 * dv * tile * float((tile_kept * rows).sum())
+        by = B * N * dqk * 2 + B * Hq * dqk * 2 + B * Hq * S * (dv + 1) * 4 + B * Hq * nk
+        out = by_block.setdefault("Bc%d" % Bc, dict(heads_per_workgroup=hg, pv_skip_unit_heads=tile,
+                                                     by_lambda={}))["by_lambda"]
+        out["%g" % lam] = dict(us=round(us, 2), us_min=round(us_lo, 2), us_max=round(us_hi, 2),
+                               GBs=round(by / us / 1e3, 1), frac_of_hbm_peak=round(by / us / 1e3 / HBM_PEAK_GBS, 4),
+                               tflops_executed=round((s_flops + pv_flops) / us / 1e6, 1),
+                               block_sparsity=round(float(sk.mean()), 5),
+                               pv_skipped_fraction=round(1.0 - float(tile_kept.mean()), 5))
+    for blk in by_block.values():
+        dense = blk["by_lambda"]["0"]["us"]
+        for v in blk["by_lambda"].values():
             v["speedup_vs_lambda0"] = round(dense / v["us"], 4)
-        by_block["Bc%d" % Bc] = dict(heads_per_workgroup=hg, pv_skip_unit_heads=tile, by_lambda=out)
     by = B * N * dqk * 2
     return dict(workload=w.name, B=B, Hq=Hq, d_qk=dqk, d_v=dv, context=N, num_splits=S, kv_copies_rotated=len(kvs),
                 by_block=by_block,
