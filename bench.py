@@ -457,38 +457,24 @@ def bench_prefill(args, lib, torch, W):
     tile_flops = 2.0 * Bc * Bc * d
     sp = ctypes.c_void_p(stream.cuda_stream)
 
-    def timed(fn, a):
-        """TRIALS trials of prefill_reps back-to-back launches (after 2 warm-ups); median, min, max in ms."""
-        for _ in range(2):
-            assert fn(*a) == 0
-        torch.cuda.synchronize()
-        ts = []
-        for _ in range(TRIALS):
-            s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            s0.record(stream)
-            for _ in range(args.prefill_reps):
-                assert fn(*a) == 0
-            s1.record(stream)
-            torch.cuda.synchronize()
-            ts.append(s0.elapsed_time(s1) / args.prefill_reps)
-        return float(np.median(ts)), min(ts), max(ts)
+    def check(st):
+        assert st == 0
 
+    # each lambda once for its mask and its error against the lambda = 0 output (untimed), then every
+    # lambda and the kernel without the skip test timed in turns, prefill_reps launches per round
+    lams = (0.0,) + tuple(w.lambdas)
     o0 = lse0 = None
-    for lam in (0.0,) + tuple(w.lambdas):
+    fns = []
+    for lam in lams:
         a = (P(x["q"]), P(x["k"]), P(x["v"]), P(o), P(lse), P(mask), B, Hq, T, d, w.G, Bc,
              ctypes.c_double(lam), 1, sp)
-        ms, ms_min, ms_max = timed(lib.blasst_prefill, a)
-        m = mask.cpu().numpy()
-        skipped = int((m == 1).sum())
-        kept = visited - skipped
-        flops = (visited + kept) * tile_flops
-        tflops = flops / (ms * 1e-3) / 1e12
-        out["%g" % lam] = dict(ms=round(ms, 4), ms_min=round(ms_min, 4), ms_max=round(ms_max, 4),
-                               tflops_executed=round(tflops, 2),
-                               frac_of_mfma_peak=round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                               block_sparsity=round(skipped / visited, 5),
-                               executed_tflop=round(flops / 1e12, 4))
-        # the skip's error against the dense (lambda = 0) output of the same kernel, untimed
+        check(lib.blasst_prefill(*a))
+        torch.cuda.synchronize()
+        fns.append(lambda a=a: check(lib.blasst_prefill(*a)))
+        skipped = int((mask == 1).sum().item())
+        out["%g" % lam] = dict(block_sparsity=round(skipped / visited, 5),
+                               executed_tflop=round((2 * visited - skipped) * tile_flops / 1e12, 4))
+        # the skip's error against the dense (lambda = 0) output of the same kernel
         if o0 is None:
             o0, lse0 = o.clone(), lse.clone()
         else:
@@ -500,12 +486,19 @@ def bench_prefill(args, lib, torch, W):
                 rows_changed=round(float((rel > 0).float().mean().item()), 5))
             del diff, rel
     del o0, lse0
+    # the kernel built without the skip test (blasst_prefill_dense): what the test costs at 0% sparsity
+    nt_a = (P(x["q"]), P(x["k"]), P(x["v"]), P(o), P(lse), B, Hq, T, d, w.G, Bc, 1, sp)
+    fns.append(lambda: check(lib.blasst_prefill_dense(*nt_a)))
+    times = interleaved_trials(torch, stream, fns, args.prefill_reps, warm=2)
+    for lam, (ms, ms_min, ms_max) in zip(lams, times):
+        v = out["%g" % lam]
+        tflops = v["executed_tflop"] * 1e12 / (ms * 1e-3) / 1e12
+        v.update(ms=round(ms, 4), ms_min=round(ms_min, 4), ms_max=round(ms_max, 4),
+                 tflops_executed=round(tflops, 2), frac_of_mfma_peak=round(tflops / MFMA_BF16_PEAK_TFLOPS, 4))
     dense = out["0"]["ms"]
     for k, v in out.items():
         v["speedup_vs_lambda0"] = round(dense / v["ms"], 4)
-    # the kernel built without the skip test (blasst_prefill_dense): what the test costs at 0% sparsity
-    ref_ms, _, _ = timed(lib.blasst_prefill_dense,
-                         (P(x["q"]), P(x["k"]), P(x["v"]), P(o), P(lse), B, Hq, T, d, w.G, Bc, 1, sp))
+    ref_ms = times[-1][0]
     no_test = dict(ms=round(ref_ms, 4), tflops=round(2 * visited * tile_flops / (ref_ms * 1e-3) / 1e12, 2),
                    lambda0_speed_vs_no_test=round(ref_ms / dense, 4))
     return dict(workload=w.name, B=B, Hq=Hq, Hkv=w.Hkv, d=d, T=T, Bc=Bc, by_lambda=out, no_skip_test=no_test,
