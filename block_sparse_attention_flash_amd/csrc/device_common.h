@@ -90,11 +90,12 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // wait states this family needs before it are in the asm itself: one after a
 // scalar write of M0 (which the compiler emits right before the asm).
 // STREAM sets the non-temporal cache policy (nt), for rows that one pass reads
-// once: the decode kernels' K and V.  A 134 MB decode pass runs 8% faster with
-// it (a plain streaming read of that size runs 5.6-5.9 TB/s with ordinary loads
-// and 6.1-6.5 TB/s with non-temporal ones).  The prefill tiles, which the query
-// blocks of a kv head share in L2, keep the default policy (non-temporal,
-// prefill ran 3% slower).
+// once and no other workgroup needs from L2 later: the decode kernels' V, and
+// their K where no partner workgroup re-reads it (decode.hip says where).  A
+// 134 MB decode pass runs 8% faster with it (a plain streaming read of that size
+// runs 5.6-5.9 TB/s with ordinary loads and 6.1-6.5 TB/s with non-temporal
+// ones).  The prefill tiles, which the query blocks of a kv head share in L2,
+// keep the default policy (non-temporal, prefill ran 3% slower).
 template <bool STREAM = false>
 __device__ __forceinline__ void global_to_lds16(const void* gptr, uint32_t lds_base) {
     if constexpr (STREAM)
