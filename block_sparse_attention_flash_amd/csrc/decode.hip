@@ -84,7 +84,6 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
     constexpr int UPP = W * UW;           // units per phase
     constexpr int BPP = UPP / KG;         // blocks per phase
     constexpr int DS = D / 32;            // MFMA k-steps over d for S
-    constexpr int DT = D / 16;            // 16-wide d tiles of O^T
     constexpr int FR = D / 16;            // 16-byte fragments per lane per unit
     constexpr int CPR = D / 8;            // 16-byte chunks per K/V row
     constexpr int HT = 16 * NT;           // head columns per workgroup
@@ -828,7 +827,7 @@ __global__ __launch_bounds__(512) void decode_wide_kernel(DecodeArgs a) {
                     if (c < cnt) a.skip[((size_t)b * a.Hq + (size_t)hkv * G + h) * nk + base + c] = lds_mask[c][h];
                 }
             }
-            if (a.vskip != nullptr && threadIdx.x < cnt)
+            if (a.vskip != nullptr && (int)threadIdx.x < cnt)
                 a.vskip[((size_t)b * a.Hkv + hkv) * nk + base + threadIdx.x] = lds_vmask[threadIdx.x];
         }
 

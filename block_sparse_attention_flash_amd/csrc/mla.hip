@@ -326,7 +326,8 @@ __global__ __launch_bounds__(512) void mla_split_kernel(MlaArgs a) {
 // the S MFMAs of one block overlap the P V MFMAs of the previous one.
 template <int BCM>
 __global__ __launch_bounds__(512) void mla_pipe_kernel(MlaArgs a) {
-    constexpr int W = 8;
+    constexpr int W = 8;                         // waves: four of each role
+    static_assert(64 * W == 512, "the launch bounds hold eight waves");
     constexpr int SB = 32;                       // tokens per sub-block (one pipeline step)
     constexpr int HPB = BCM / SB;                // sub-blocks per decision block
     constexpr int HG = 64;                       // heads per workgroup
