@@ -380,21 +380,6 @@ def bench_decode(args, lib, torch, W):
         torch.cuda.synchronize()
         return start.elapsed_time(stop) / args.steps
 
-    def kernel_trials(fn_args, reps):
-        """TRIALS trials of reps back-to-back launches of one kernel: median, min, max in ms."""
-        for s in range(4):
-            fn_args(s)
-        torch.cuda.synchronize()
-        ts = []
-        for _ in range(TRIALS):
-            start.record(stream)
-            for s in range(reps):
-                fn_args(s)
-            stop.record(stream)
-            torch.cuda.synchronize()
-            ts.append(start.elapsed_time(stop) / reps)
-        return float(np.median(ts)), min(ts), max(ts)
-
     # the same kernel at lambda = 0 (nothing skipped; the test and the decision bytes still run)
     lambda0_step_ms = step_time(lambda s: check(decode_fn(*dense_args[s % len(dense_args)])))
     # the dense kernel (blasst_decode_dense: one pass over K and V, no decision)
@@ -402,12 +387,9 @@ def bench_decode(args, lib, torch, W):
     ref_fn = lambda s: check(lib.blasst_decode_dense(*ref_args[s % len(ref_args)]))  # noqa: E731
     dense_step_ms = step_time(ref_fn)
     reps = max(args.steps, 50)
-    dense_kernel_ms = kernel_trials(ref_fn, reps)
     # the split kernel's loads alone at lambda = 0 (blasst_decode_load_ceiling): the floor its bytes and
     # its access pattern set on this part
     ceil_args = [(P(c["k"]), P(c["v"]), B, w.Hkv, N, d, Bc, S, sp) for c in copies]
-    load_ceiling_ms = kernel_trials(lambda s: check(lib.blasst_decode_load_ceiling(*ceil_args[s % len(ceil_args)])),
-                                    reps)
 
     # decisions of the timed configuration (identical on every copy)
     check(decode_fn(*sargs[0]))
@@ -415,15 +397,30 @@ def bench_decode(args, lib, torch, W):
     sk, vsk = skip.cpu().numpy(), vskip.cpu().numpy()
     by = decode_bytes(w, vsk)
 
-    # lambda sweep on the same inputs: the split kernel against the dense kernel
-    sweep = []
+    def rotating(launch):
+        """A callable launching launch(i) with i = 0, 1, 2, ... (the KV copies rotate with i)."""
+        it = [0]
+
+        def f():
+            launch(it[0])
+            it[0] += 1
+        return f
+
+    # lambda sweep on the same inputs: each lambda once for its decisions, then the dense kernel, the
+    # load ceiling and every lambda timed in turns (reps launches per case and round)
     dense_by = decode_bytes(w, np.zeros_like(vsk))
+    fns = [rotating(ref_fn), rotating(lambda s: check(lib.blasst_decode_load_ceiling(*ceil_args[s % len(ceil_args)])))]
+    stats = []
     for lam_ in DECODE_SWEEP_LAMBDAS:
         la = [split_args(c, lam_) for c in copies]
-        ms = kernel_trials(lambda s: check(decode_fn(*la[s % len(la)])), reps)
         check(decode_fn(*la[0]))
         torch.cuda.synchronize()
-        sk_, vsk_ = skip.cpu().numpy(), vskip.cpu().numpy()
+        stats.append((skip.cpu().numpy(), vskip.cpu().numpy()))
+        fns.append(rotating(lambda s, la=la: check(decode_fn(*la[s % len(la)]))))
+    times = interleaved_trials(torch, stream, fns, reps, warm=4)
+    dense_kernel_ms, load_ceiling_ms = times[0], times[1]
+    sweep = []
+    for lam_, (sk_, vsk_), ms in zip(DECODE_SWEEP_LAMBDAS, stats, times[2:]):
         by_ = decode_bytes(w, vsk_)
         sweep.append(dict(
             lam=lam_, split_kernel_us=round(ms[0] * 1e3, 3), split_kernel_us_min=round(ms[1] * 1e3, 3),
