@@ -37,6 +37,9 @@
 //           same slots and are read back transposed (ds_read_b64_tr_b16) as
 //           the A operand of O^T += V^T P^T.  P^T is the S^T accumulator (same
 //           lane layout) after 2^(t - m), rounded to bf16.
+// Cache policy of the copies: V non-temporal; K non-temporal except where the
+// other workgroup of a pair, or another head part, reads it again from L2 (the
+// K pass says where).
 // Scores are kept in log2 units (t = s * log2(e)), so P uses v_exp_f32 directly
 // and the test reads t~ - m < ln(lambda) * log2(e).
 #include "device_common.h"
@@ -998,8 +1001,8 @@ __global__ __launch_bounds__(64 * W) void decode_dense_kernel(DecodeArgs a) {
     // unit u of this wave: keys key_base + 32 (wave + W u) ..; slot pair u % NSLOT
     auto pair_of = [&](int u) { return lds_kv + (NSLOT * wave + u % NSLOT) * PAIR; };
     // V non-temporal as in the split kernel; K on the default cache policy, with
-    // which this kernel ran 4% faster (the split kernel runs faster with K
-    // non-temporal too)
+    // which this kernel ran 4% faster (the split kernel, unlike this one, runs
+    // faster with K non-temporal)
     auto issue = [&](int u) {
         const int key0 = key_base + 32 * (wave + W * u);
         const char* slot = pair_of(u);
